@@ -1,0 +1,55 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle side.
+
+This module holds no attention arithmetic: it draws numbers and rounds them
+to bfloat16.  Both the HIP path and the CPU oracle receive exactly the arrays
+it returns (the oracle as their exact float64 values).
+
+Recipe: NumPy PCG64 ``default_rng(seed)``, ``standard_normal(shape,
+dtype=float32)`` drawn in the order the caller lists the tensors (Q, K, V,
+then dO), each rounded to bfloat16 with round-to-nearest-even on the upper 16
+bits.  N(0, 1) values never round to NaN or Inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def seeded_bf16(seed: int, shapes) -> list[np.ndarray]:
+    """Draw one N(0,1) float32 tensor per shape from one PCG64 stream, rounded to bf16 bits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for shape in shapes:
+        x = rng.standard_normal(tuple(shape), dtype=np.float32)
+        out.append(f32_to_bf16_bits(x))
+    return out
+
+
+def attention_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int,
+                     with_grad: bool = False) -> list[np.ndarray]:
+    """bf16 bit arrays Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO [B,Hq,N,d])."""
+    shapes = [(B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)]
+    if with_grad:
+        shapes.append((B, Hq, N, d))
+    return seeded_bf16(seed, shapes)

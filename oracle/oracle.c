@@ -1,0 +1,326 @@
+/*
+ * oracle.c -- plain fp64 CPU definition of exact attention and its gradients.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * HIP library.
+ *
+ * What it computes (per batch b and query head hq; the key/value head is
+ * hk = hq / (Hq/Hkv)):
+ *
+ *   S_ij = scale * sum_t Q_it K_jt                      (scores, scaled)
+ *   S_ij = -inf  for j > i when causal                  (mask after scaling)
+ *   L_i  = m_i + ln sum_j exp(S_ij - m_i),  m_i = max_j S_ij
+ *   P_ij = exp(S_ij - L_i)
+ *   O_i  = sum_j P_ij V_j
+ *
+ * and, given dO, the gradients of sum(dO * O):
+ *
+ *   dP_ij = sum_t dO_it V_jt
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij K_j
+ *   dK_j  = scale * sum_{hq in group} sum_i dS_ij Q_i
+ *   dV_j  =         sum_{hq in group} sum_i P_ij dO_i
+ *
+ * Sources (FlashAttention-2 summary page, zhaifeiyue.github.io, section 3
+ * "Target operation" for O = softmax(QK^T)V with optional causal mask and
+ * FP16/BF16 inputs; section 4 symbol table for L = m + log(l) and
+ * D = rowsum(dO o O); section 4 "checks" for exactness and for GQA/MQA
+ * sharing K/V heads with dK/dV summed across the sharing heads; section 3
+ * FLOP formula for the five backward matmuls).  The pages do not print the
+ * backward formulas beyond D and P = exp(S - L); the ones above follow from
+ * differentiating the definition.  The scale multiplies the scores before
+ * masking and the softmax; L is a natural-log logsumexp of the scaled,
+ * masked scores.
+ *
+ * This is the definition, evaluated directly: every row of S is formed in
+ * full, its true maximum is taken in one pass, and no online or tiled
+ * softmax is used.  Sums run in index order in double precision.  No BLAS.
+ *
+ * Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV
+ * (H = Hq for Q/O/dO/dQ, H = Hkv for K/V/dK/dV); [B, Hq, N] for L and D.
+ *
+ * Return value of every entry point: 0 on success, -1 on bad sizes
+ * (negative sizes, Hq not a multiple of Hkv, d < 1 when there is work).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int check_sizes(int B, int Hq, int Hkv, int N, int d)
+{
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return -1;
+    if (Hkv == 0) return (Hq == 0) ? 0 : -1;
+    if (Hq % Hkv != 0) return -1;
+    if (d < 1 && (long)B * Hq * N > 0) return -1;
+    return 0;
+}
+
+static const double *head_ptr(const double *X, int b, int h, int H, int N, int d)
+{
+    return X + (((size_t)b * H + h) * (size_t)N) * (size_t)d;
+}
+
+/* Scaled, masked score S_ij of one query row q (length d) against key row k. */
+static double score(const double *q, const double *k, int d, double scale,
+                    int causal, int i, int j)
+{
+    if (causal && j > i) return -INFINITY;
+    double acc = 0.0;
+    for (int t = 0; t < d; ++t) acc += q[t] * k[t];
+    return scale * acc;
+}
+
+/*
+ * Row i of one head: fills s[0..N) with the scaled masked scores and returns
+ * L_i = m + ln sum_j exp(s_j - m).  The causal mask keeps j <= i, so every
+ * row has at least one finite score (j = 0).
+ */
+static double row_scores_lse(const double *Qh, const double *Kh, int N, int d,
+                             double scale, int causal, int i, double *s)
+{
+    const double *q = Qh + (size_t)i * d;
+    double m = -INFINITY;
+    for (int j = 0; j < N; ++j) {
+        s[j] = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
+        if (s[j] > m) m = s[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < N; ++j) sum += exp(s[j] - m);
+    return m + log(sum);
+}
+
+/* Forward of one query row: O_i (length d) and L_i. */
+static double row_forward(const double *Qh, const double *Kh, const double *Vh,
+                          int N, int d, double scale, int causal, int i,
+                          double *s, double *o)
+{
+    double L = row_scores_lse(Qh, Kh, N, d, scale, causal, i, s);
+    for (int t = 0; t < d; ++t) o[t] = 0.0;
+    for (int j = 0; j < N; ++j) {
+        double p = exp(s[j] - L);
+        if (p == 0.0) continue;              /* masked (exp(-inf) = 0) */
+        const double *v = Vh + (size_t)j * d;
+        for (int t = 0; t < d; ++t) o[t] += p * v[t];
+    }
+    return L;
+}
+
+int oracle_fwd(const double *Q, const double *K, const double *V, double *O,
+               double *L, int B, int Hq, int Hkv, int N, int d, int causal,
+               double scale)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if ((long)B * Hq * N == 0) return 0;
+    const int G = Hq / Hkv;
+    const long rows = (long)B * Hq * N;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(dynamic, 16)
+        for (long r = 0; r < rows; ++r) {
+            int i = (int)(r % N);
+            int hq = (int)((r / N) % Hq);
+            int b = (int)(r / ((long)N * Hq));
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);
+            const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);
+            double *o = O + (size_t)r * d;
+            double l = row_forward(Qh, Kh, Vh, N, d, scale, causal, i, s, o);
+            if (L) L[r] = l;
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * Forward of selected rows only: row r of the output is query row ri[r] of
+ * head (rb[r], rh[r]).  O_rows is [n, d], L_rows is [n].  Used to check
+ * outputs of large problems one row at a time.
+ */
+int oracle_fwd_rows(const double *Q, const double *K, const double *V,
+                    int B, int Hq, int Hkv, int N, int d, int causal,
+                    double scale, int n, const int *rb, const int *rh,
+                    const int *ri, double *O_rows, double *L_rows)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    for (int r = 0; r < n; ++r)
+        if (rb[r] < 0 || rb[r] >= B || rh[r] < 0 || rh[r] >= Hq ||
+            ri[r] < 0 || ri[r] >= N) return -1;
+    if (n == 0) return 0;
+    const int G = Hq / Hkv;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n; ++r) {
+            const double *Qh = head_ptr(Q, rb[r], rh[r], Hq, N, d);
+            const double *Kh = head_ptr(K, rb[r], rh[r] / G, Hkv, N, d);
+            const double *Vh = head_ptr(V, rb[r], rh[r] / G, Hkv, N, d);
+            double l = row_forward(Qh, Kh, Vh, N, d, scale, causal, ri[r], s,
+                                   O_rows + (size_t)r * d);
+            if (L_rows) L_rows[r] = l;
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * Backward of one key/value head (b, hk) and the G query heads that share it.
+ *   dQg [G, N, d]  dQ of query heads hk*G .. hk*G+G-1
+ *   dKh, dVh [N, d]
+ *   Lg, Dg [G, N]  the statistics L and D of those query heads (may be NULL)
+ * Three passes, each over the plain definitions: row statistics, then dQ by
+ * rows, then dK/dV by key columns (so no two threads write one location).
+ */
+static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
+                            const double *dO, int Hq, int Hkv, int N, int d,
+                            int causal, double scale, int b, int hk,
+                            double *dQg, double *dKh, double *dVh,
+                            double *Lg, double *Dg)
+{
+    const int G = Hq / Hkv;
+    const double *Kh = head_ptr(K, b, hk, Hkv, N, d);
+    const double *Vh = head_ptr(V, b, hk, Hkv, N, d);
+    double *Lst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    double *Dst = (double *)malloc(sizeof(double) * (size_t)G * N);
+
+    /* Pass 1: L_i and D_i = sum_j P_ij dP_ij for every query row. */
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(dynamic, 8)
+        for (long r = 0; r < (long)G * N; ++r) {
+            int g = (int)(r / N), i = (int)(r % N);
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+            double L = row_scores_lse(Qh, Kh, N, d, scale, causal, i, s);
+            double D = 0.0;
+            for (int j = 0; j < N; ++j) {
+                double p = exp(s[j] - L);
+                if (p == 0.0) continue;
+                const double *v = Vh + (size_t)j * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                D += p * dp;
+            }
+            Lst[r] = L;
+            Dst[r] = D;
+        }
+        free(s);
+    }
+
+    /* Pass 2: dQ_i = scale * sum_j dS_ij K_j. */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (long r = 0; r < (long)G * N; ++r) {
+            int g = (int)(r / N), i = (int)(r % N);
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *q = Qh + (size_t)i * d;
+            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+            double *dq = dQg + (size_t)r * d;
+            for (int t = 0; t < d; ++t) dq[t] = 0.0;
+            for (int j = 0; j < N; ++j) {
+                double sij = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
+                double p = exp(sij - Lst[r]);
+                if (p == 0.0) continue;
+                const double *v = Vh + (size_t)j * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                double ds = p * (dp - Dst[r]);
+                const double *k = Kh + (size_t)j * d;
+                for (int t = 0; t < d; ++t) dq[t] += ds * k[t];
+            }
+            for (int t = 0; t < d; ++t) dq[t] *= scale;
+    }
+
+    /* Pass 3: dK_j = scale * sum_g sum_i dS_ij Q_i ;  dV_j = sum_g sum_i P_ij dO_i. */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int j = 0; j < N; ++j) {
+        const double *k = Kh + (size_t)j * d;
+        const double *v = Vh + (size_t)j * d;
+        double *dk = dKh + (size_t)j * d;
+        double *dv = dVh + (size_t)j * d;
+        for (int t = 0; t < d; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
+        for (int g = 0; g < G; ++g) {
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
+            for (int i = 0; i < N; ++i) {
+                const double *q = Qh + (size_t)i * d;
+                double sij = score(q, k, d, scale, causal, i, j);
+                double p = exp(sij - Lst[(long)g * N + i]);
+                if (p == 0.0) continue;
+                const double *dOr = dOh + (size_t)i * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                double ds = p * (dp - Dst[(long)g * N + i]);
+                for (int t = 0; t < d; ++t) {
+                    dv[t] += p * dOr[t];
+                    dk[t] += ds * q[t];
+                }
+            }
+        }
+        for (int t = 0; t < d; ++t) dk[t] *= scale;
+    }
+
+    if (Lg) memcpy(Lg, Lst, sizeof(double) * (size_t)G * N);
+    if (Dg) memcpy(Dg, Dst, sizeof(double) * (size_t)G * N);
+    free(Lst);
+    free(Dst);
+}
+
+int oracle_bwd(const double *Q, const double *K, const double *V,
+               const double *dO, double *dQ, double *dK, double *dV,
+               double *D, int B, int Hq, int Hkv, int N, int d, int causal,
+               double scale)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if ((long)B * Hq * N == 0) return 0;
+    const int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b)
+        for (int hk = 0; hk < Hkv; ++hk) {
+            size_t qoff = (((size_t)b * Hq + (size_t)hk * G) * N) * d;
+            size_t koff = (((size_t)b * Hkv + hk) * (size_t)N) * d;
+            double *Dg = D ? D + ((size_t)b * Hq + (size_t)hk * G) * N : NULL;
+            bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+                            dQ + qoff, dK + koff, dV + koff, NULL, Dg);
+        }
+    return 0;
+}
+
+/*
+ * Backward restricted to one key/value head (b, hk): dQg [G,N,d] for query
+ * heads hk*G.., dKh/dVh [N,d], and optionally Lg/Dg [G,N].  Used to check
+ * single heads of large problems.
+ */
+int oracle_bwd_head(const double *Q, const double *K, const double *V,
+                    const double *dO, int B, int Hq, int Hkv, int N, int d,
+                    int causal, double scale, int b, int hk, double *dQg,
+                    double *dKh, double *dVh, double *Lg, double *Dg)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if (b < 0 || b >= B || hk < 0 || hk >= Hkv) return -1;
+    if (N == 0) return 0;
+    bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+                    dQg, dKh, dVh, Lg, Dg);
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,47 @@
+"""Host-side helpers: seeded bf16 inputs and FLOP accounting (CPU only)."""
+import json
+import os
+
+import numpy as np
+import torch
+
+from exact_io_aware_26_amd import inputs, workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.005859375, 3.0e38, -3.0e38, 1e-40, np.inf, -np.inf],
+                 dtype=np.float32),
+    ])
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = inputs.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_seeded_inputs_are_reproducible_and_ordered():
+    a = inputs.attention_inputs(5, 1, 2, 1, 8, 4, with_grad=True)
+    b = inputs.attention_inputs(5, 1, 2, 1, 8, 4, with_grad=True)
+    assert [x.shape for x in a] == [(1, 2, 8, 4), (1, 1, 8, 4), (1, 1, 8, 4), (1, 2, 8, 4)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 2, 8, 4), dtype=np.float32)
+    assert np.array_equal(a[0], inputs.f32_to_bf16_bits(q))
+    vals = inputs.bf16_bits_to_f32(a[1])
+    assert np.all(np.isfinite(vals))
+
+
+def test_flop_accounting_matches_golden():
+    with open(os.path.join(GOLDEN, "flops.json")) as f:
+        g = json.load(f)
+    for name, want in g["fwd"].items():
+        assert workloads.BY_NAME[name].fwd_flops() == want, name
+    for name, want in g["bwd"].items():
+        assert workloads.BY_NAME[name].bwd_flops() == want, name

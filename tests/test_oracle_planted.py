@@ -1,0 +1,64 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies ``oracle/oracle.c``, plants one plausible mistake by a
+textual replacement (a dropped term, a wrong sign, an off-by-one mask, a
+wrong index or a transposed operand), compiles the copy, and checks that at
+least one pin fails on it.  The real oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+from oracle import oracle as orc
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+MUTATIONS = [
+    ("scale dropped from the scores", "return scale * acc;", "return acc;"),
+    ("causal mask off by one", "if (causal && j > i) return -INFINITY;",
+     "if (causal && j > i + 1) return -INFINITY;"),
+    ("log2 instead of natural log in L", "return m + log(sum);", "return m + log2(sum);"),
+    ("row maximum not subtracted inside the sum", "sum += exp(s[j] - m);", "sum += exp(s[j]);"),
+    ("wrong GQA head mapping in the forward",
+     "const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);",
+     "const double *Kh = head_ptr(K, b, hq % Hkv, Hkv, N, d);"),
+    ("value row index i instead of j", "const double *v = Vh + (size_t)j * d;\n        for (int t = 0; t < d; ++t) o[t] += p * v[t];",
+     "const double *v = Vh + (size_t)i * d;\n        for (int t = 0; t < d; ++t) o[t] += p * v[t];"),
+    ("D dropped from dS in dQ", "double ds = p * (dp - Dst[r]);", "double ds = p * dp;"),
+    ("wrong sign of dS in dK", "double ds = p * (dp - Dst[(long)g * N + i]);",
+     "double ds = p * (Dst[(long)g * N + i] - dp);"),
+    ("D without the P weight", "D += p * dp;", "D += dp;"),
+    ("dQ built from Q instead of K", "for (int t = 0; t < d; ++t) dq[t] += ds * k[t];",
+     "for (int t = 0; t < d; ++t) dq[t] += ds * q[t];"),
+    ("scale missing from dK", "for (int t = 0; t < d; ++t) dk[t] *= scale;", ""),
+    ("dV uses the key-side row of dO (transposed operand)", "dv[t] += p * dOr[t];",
+     "dv[t] += p * dOh[(size_t)j * d + t];"),
+    ("dK sums over one query head of the group only", "for (int g = 0; g < G; ++g) {",
+     "for (int g = 0; g < 1; ++g) {"),
+]
+
+
+def _pins_fail(lib):
+    failures = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError) as e:
+            failures.append(f"{pin.__name__}: {str(e)[:80]}")
+    return failures
+
+
+@pytest.mark.parametrize("desc,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(desc, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = str(tmp_path / "liboracle_mutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-w",
+                    "-o", so, str(mutated), "-lm"], check=True)
+    lib = orc.load(so)
+    failures = _pins_fail(lib)
+    assert failures, f"planted mistake '{desc}' passed every pin"
