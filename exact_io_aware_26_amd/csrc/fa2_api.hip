@@ -1,0 +1,264 @@
+// fa2_api.hip -- the C ABI of libfa2.so (declared in include/fa2.h).
+//
+// Argument checking is pure host code that makes no HIP call, so it is
+// testable without a GPU (fa2_validate_fwd / fa2_validate_bwd).  The entry
+// points check, then fill the kernel parameter blocks and launch on the
+// caller's stream.  The library allocates nothing: the backward pass's
+// fp32 scratch (D and the dQ accumulator) comes from the caller's workspace.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa2.h"
+#include "fa2_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+fa2_status fail(fa2_status s, const char* fmt, const char* detail = nullptr) {
+    if (detail)
+        std::snprintf(g_last_error, sizeof g_last_error, fmt, detail);
+    else
+        std::snprintf(g_last_error, sizeof g_last_error, "%s", fmt);
+    return s;
+}
+
+constexpr size_t kWorkspaceAlign = 256;
+constexpr int kMaxN = 1 << 30;             // keeps every in-kernel row index in int range
+constexpr uint64_t kMaxGridThreads = 0xFFFFFFFFull;  // work-items per grid dimension
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool mul_overflows(uint64_t a, uint64_t b, uint64_t* out) {
+    if (a != 0 && b > UINT64_MAX / a) return true;
+    *out = a * b;
+    return false;
+}
+
+// Element count of [a, b, c, d]; false on 64-bit overflow.
+bool count4(int a, int b, int c, int d, uint64_t* out) {
+    uint64_t x;
+    if (mul_overflows((uint64_t)a, (uint64_t)b, &x)) return false;
+    if (mul_overflows(x, (uint64_t)c, &x)) return false;
+    if (mul_overflows(x, (uint64_t)d, &x)) return false;
+    *out = x;
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bbytes && y < x + abytes;
+}
+
+struct Sizes {
+    uint64_t q_elems = 0, kv_elems = 0, rows = 0;  // rows = B * Hq * N
+};
+
+// Shared checks of sizes, head dim, scale and grid limits.  Returns FA2_OK
+// with *empty set when there is nothing to compute.
+fa2_status check_problem(int B, int Hq, int Hkv, int N, int d, float scale, bool* empty,
+                         Sizes* sz) {
+    *empty = false;
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0)
+        return fail(FA2_ERR_INVALID_ARGUMENT, "negative size");
+    if (B == 0 || Hq == 0 || N == 0) {
+        *empty = true;
+        return FA2_OK;
+    }
+    if (Hkv < 1) return fail(FA2_ERR_INVALID_ARGUMENT, "Hkv must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA2_ERR_INVALID_ARGUMENT, "Hq must be a multiple of Hkv");
+    if (d != 64 && d != 128 && d != 256)
+        return fail(FA2_ERR_UNSUPPORTED, "head dim must be 64, 128 or 256");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (!count4(B, Hq, N, d, &sz->q_elems) || !count4(B, Hkv, N, d, &sz->kv_elems) ||
+        !count4(B, Hq, N, 1, &sz->rows) || sz->q_elems > (UINT64_MAX >> 3))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "element count overflows 64 bits");
+    if (N > kMaxN) return fail(FA2_ERR_UNSUPPORTED, "N above 2^30");
+    // Largest grid launched: forward B*Hq*ceil(N/128) or backward B*Hkv*ceil(N/64), 256 threads.
+    const uint64_t tiles = (uint64_t)B * (uint64_t)Hq * (uint64_t)((N + 63) / 64);
+    if (tiles * 256u > kMaxGridThreads) return fail(FA2_ERR_UNSUPPORTED, "grid too large");
+    return FA2_OK;
+}
+
+fa2_status validate_fwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                        int B, int Hq, int Hkv, int N, int d, float scale, bool* empty, Sizes* sz) {
+    fa2_status s = check_problem(B, Hq, Hkv, N, d, scale, empty, sz);
+    if (s != FA2_OK || *empty) return s;
+    const void* ptrs[5] = {Q, K, V, O, L};
+    const char* names[5] = {"Q", "K", "V", "O", "L"};
+    for (int i = 0; i < 5; ++i) {
+        if (!ptrs[i]) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i])) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    }
+    const uint64_t qb = sz->q_elems * 2, kb = sz->kv_elems * 2, lb = sz->rows * 4;
+    if (overlaps(O, qb, Q, qb) || overlaps(O, qb, K, kb) || overlaps(O, qb, V, kb))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "O aliases an input");
+    if (overlaps(L, lb, Q, qb) || overlaps(L, lb, K, kb) || overlaps(L, lb, V, kb))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "L aliases an input");
+    if (overlaps(O, qb, L, lb)) return fail(FA2_ERR_INVALID_ARGUMENT, "O aliases L");
+    return FA2_OK;
+}
+
+struct WorkspaceLayout {
+    size_t d_off, dq_off, total;
+};
+
+WorkspaceLayout workspace_layout(uint64_t rows, uint64_t q_elems) {
+    WorkspaceLayout w;
+    w.d_off = 0;
+    w.dq_off = align_up(rows * 4, kWorkspaceAlign);
+    w.total = w.dq_off + align_up(q_elems * 4, kWorkspaceAlign);
+    return w;
+}
+
+fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                        const void* dO, const void* dQ, const void* dK, const void* dV,
+                        const void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
+                        float scale, bool* empty, Sizes* sz) {
+    fa2_status s = check_problem(B, Hq, Hkv, N, d, scale, empty, sz);
+    if (s != FA2_OK || *empty) return s;
+    const void* ptrs[9] = {Q, K, V, O, L, dO, dQ, dK, dV};
+    const char* names[9] = {"Q", "K", "V", "O", "L", "dO", "dQ", "dK", "dV"};
+    for (int i = 0; i < 9; ++i) {
+        if (!ptrs[i]) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i])) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    }
+    if (!ws) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) != 0)
+        return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    const WorkspaceLayout wl = workspace_layout(sz->rows, sz->q_elems);
+    if (ws_bytes < wl.total) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace too small");
+    const uint64_t qb = sz->q_elems * 2, kb = sz->kv_elems * 2, lb = sz->rows * 4;
+    const void* ins[6] = {Q, K, V, O, L, dO};
+    const uint64_t in_bytes[6] = {qb, kb, kb, qb, lb, qb};
+    const void* outs[4] = {dQ, dK, dV, ws};
+    const uint64_t out_bytes[4] = {qb, kb, kb, wl.total};
+    const char* out_names[4] = {"dQ", "dK", "dV", "workspace"};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i]))
+                return fail(FA2_ERR_INVALID_ARGUMENT, "%s aliases an input", out_names[o]);
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2]))
+                return fail(FA2_ERR_INVALID_ARGUMENT, "%s aliases another output", out_names[o]);
+    }
+    return FA2_OK;
+}
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa2_status_string(fa2_status s) {
+    switch (s) {
+        case FA2_OK: return "FA2_OK";
+        case FA2_ERR_INVALID_ARGUMENT: return "FA2_ERR_INVALID_ARGUMENT";
+        case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED";
+        case FA2_ERR_HIP: return "FA2_ERR_HIP";
+    }
+    return "unknown status";
+}
+
+const char* fa2_last_error(void) { return g_last_error; }
+
+fa2_status fa2_validate_fwd(const void* Q, const void* K, const void* V, const void* O,
+                            const float* L, int B, int Hq, int Hkv, int N, int d, int causal,
+                            float scale) {
+    (void)causal;
+    g_last_error[0] = '\0';
+    bool empty;
+    Sizes sz;
+    return validate_fwd(Q, K, V, O, L, B, Hq, Hkv, N, d, scale, &empty, &sz);
+}
+
+fa2_status fa2_validate_bwd(const void* Q, const void* K, const void* V, const void* O,
+                            const float* L, const void* dO, const void* dQ, const void* dK,
+                            const void* dV, const void* workspace, size_t workspace_bytes, int B,
+                            int Hq, int Hkv, int N, int d, int causal, float scale) {
+    (void)causal;
+    g_last_error[0] = '\0';
+    bool empty;
+    Sizes sz;
+    return validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq, Hkv, N,
+                        d, scale, &empty, &sz);
+}
+
+size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return 0;
+    if (B == 0 || Hq == 0 || N == 0) return 0;
+    if (Hkv < 1 || Hq % Hkv != 0) return 0;
+    uint64_t q_elems, rows;
+    if (!count4(B, Hq, N, d, &q_elems) || !count4(B, Hq, N, 1, &rows) ||
+        q_elems > (UINT64_MAX >> 3))
+        return 0;
+    return workspace_layout(rows, q_elems).total;
+}
+
+fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale, void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    Sizes sz;
+    fa2_status s = validate_fwd(Q, K, V, O, L, B, Hq, Hkv, N, d, scale, &empty, &sz);
+    if (s != FA2_OK || empty) return s;
+    fa2::FwdParams p;
+    p.Q = static_cast<const uint16_t*>(Q);
+    p.K = static_cast<const uint16_t*>(K);
+    p.V = static_cast<const uint16_t*>(V);
+    p.O = static_cast<uint16_t*>(O);
+    p.L = L;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.G = Hq / Hkv;
+    p.n_qtiles = (N + fa2::kFwdRows - 1) / fa2::kFwdRows;
+    p.c = (float)((double)scale * kLog2e);
+    hipError_t e = fa2::launch_fwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
+    return FA2_OK;
+}
+
+fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                   const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                   size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float scale, void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    Sizes sz;
+    fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
+                                Hkv, N, d, scale, &empty, &sz);
+    if (s != FA2_OK || empty) return s;
+    const WorkspaceLayout wl = workspace_layout(sz.rows, sz.q_elems);
+    fa2::BwdParams p;
+    p.Q = static_cast<const uint16_t*>(Q);
+    p.K = static_cast<const uint16_t*>(K);
+    p.V = static_cast<const uint16_t*>(V);
+    p.O = static_cast<const uint16_t*>(O);
+    p.L = L;
+    p.dO = static_cast<const uint16_t*>(dO);
+    p.dQ = static_cast<uint16_t*>(dQ);
+    p.dK = static_cast<uint16_t*>(dK);
+    p.dV = static_cast<uint16_t*>(dV);
+    p.Dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.d_off);
+    p.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.G = Hq / Hkv;
+    p.scale = scale;
+    p.c = (float)((double)scale * kLog2e);
+    hipError_t e = fa2::launch_bwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
+    return FA2_OK;
+}
+
+}  // extern "C"

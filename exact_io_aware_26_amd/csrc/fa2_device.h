@@ -1,0 +1,94 @@
+// fa2_device.h -- gfx950 device helpers shared by the forward and backward kernels.
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, wave64), verified on the
+// hardware for the output layout:
+//   A operand (32 x 16, row i, reduction index k): lane l holds row i = l % 32
+//     and the 8 reduction elements of lane group g = l / 32.
+//   B operand (16 x 32, reduction index k, column j): lane l holds column
+//     j = l % 32 and the same 8 reduction elements of group g.
+//   C/D (32 x 32 fp32, 16 registers): register r of lane l is element
+//     (i = 8*(r/4) + 4*g + r%4, j = l % 32).
+// The reduction elements a lane holds only have to agree between A and B,
+// so every kernel here picks the reduction order that suits its operands.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA2_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// lo + hi of a packed bf16 pair added into an fp32 accumulator (v_dot2c_f32_bf16 with ones).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
+// Combine lane l with lane l ^ 32 (v_permlane32_swap of a register with itself
+// yields {low half, low half} and {high half, high half}).
+__device__ __forceinline__ float max_halves(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte LDS load / store.
+__device__ __forceinline__ u32x4 lds_load16(const FA2_LDS char* p) {
+    return *reinterpret_cast<const FA2_LDS u32x4*>(p);
+}
+__device__ __forceinline__ void lds_store16(FA2_LDS char* p, u32x4 v) {
+    *reinterpret_cast<FA2_LDS u32x4*>(p) = v;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 4 consecutive bf16 that lane
+// 4*e + i/4 addressed, as its element e (e = 0..3).  Measured on gfx950.
+__device__ __forceinline__ s16x4 lds_load_tr(const FA2_LDS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<FA2_LDS s16x4*>(const_cast<FA2_LDS char*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 cat_tr(s16x4 a, s16x4 b) {
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 global_load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace fa2

@@ -1,0 +1,310 @@
+// fa2_fwd.hip -- FlashAttention-2 forward pass for gfx950.
+//
+// Method (FlashAttention-2 summary page, zhaifeiyue.github.io, section 2
+// "Q2 method" and section 3): the outer loop is over blocks of query rows,
+// one workgroup each (grid = batch x heads x query tiles); the inner loop
+// streams K/V tiles.  Each wavefront owns its own slice of query rows and
+// reads the shared K/V tile from LDS, so wavefronts never exchange partial
+// results ("split-Q").  The softmax is online with a deferred rescale: the
+// accumulator holds the unnormalized sum diag(exp(m_old - m_new)) O~ +
+// exp(S - m_new) V and is divided by the row sum l once at the end; the
+// only statistic written is L = m + log(l).  With a causal mask, tiles that
+// lie wholly above the diagonal are skipped and only tiles that straddle it
+// (or the ragged end of the sequence) are masked.
+//
+// gfx950 mapping (one workgroup = 4 wave64s = 128 query rows):
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: the B operand is the wave's 32 query rows
+//     (kept in VGPRs for the whole loop) and the A operand is K read from
+//     LDS.  The accumulator layout then gives each lane ONE query row and 16
+//     keys per 32-key block, so the row max and row sum are in-lane
+//     reductions plus one v_permlane32_swap with lane l ^ 32.
+//   * The output is accumulated transposed too, O^T = V^T P^T: P^T is the
+//     score accumulator converted to bf16 in place (no data movement, the
+//     accumulator layout IS the B-operand layout), and V^T fragments come
+//     from a row-major V tile through ds_read_b64_tr_b16.  Each lane again
+//     owns one query row of the output, so the rescale by exp2(m_old -
+//     m_new) is a per-lane multiply, skipped when no row's maximum moved.
+//   * Softmax runs in the log2 domain: c = scale * log2(e) is folded into
+//     one FMA per score before v_exp_f32; the row sum is taken from the fp32
+//     probabilities (before their rounding to bf16 for the PV product), so L
+//     stays accurate to fp32 even for rows with few keys.
+//   * K/V tiles are double-buffered in LDS: the next tile's global loads are
+//     in flight while the current tile is computed; one barrier per tile.
+//     LDS rows are XOR-swizzled by 16-byte chunk (no padding) so that the
+//     MFMA operand reads are free of bank conflicts.
+//   * Grid order: the causal query tiles with the most work run first, and
+//     consecutive workgroup ids walk the heads of one query-tile level, so
+//     with B*Hq a multiple of 8 all tiles of a head land on the same XCD
+//     (workgroups are dealt round-robin to the 8 XCDs) and share its L2.
+#include "fa2_device.h"
+#include "fa2_kernels.h"
+
+namespace fa2 {
+
+namespace {
+
+template <int D> struct FwdTile;
+template <> struct FwdTile<64> { static constexpr int BC = 64; };
+template <> struct FwdTile<128> { static constexpr int BC = 64; };
+template <> struct FwdTile<256> { static constexpr int BC = 32; };
+
+constexpr int kThreads = 256;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// XOR swizzles of the 16-byte chunk index within an LDS row.
+//  K rows are read as 32 rows x 32 contiguous bytes per MFMA operand;
+//  V rows as 8 rows x 64 contiguous bytes per transposed read.
+template <int D> __device__ __forceinline__ int swz_k(int row) {
+    return D == 64 ? 2 * ((row >> 1) & 3) : 2 * (row & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int row) {
+    return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3);
+}
+
+template <int D, int BC>
+struct TileLoader {
+    static constexpr int kChunksPerRow = D / 8;                 // 16-byte chunks
+    static constexpr int kPerThread = BC * D / 8 / kThreads;    // chunks per thread per tensor
+    static_assert(kPerThread >= 1 && BC * D / 8 % kThreads == 0, "tile/threads mismatch");
+    u32x4 k[kPerThread];
+    u32x4 v[kPerThread];
+
+    __device__ __forceinline__ void load(const uint16_t* Kh, const uint16_t* Vh, int kv0, int N,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = c / kChunksPerRow;
+            const int col = c % kChunksPerRow;
+            const int gr = kv0 + row;
+            if (gr < N) {
+                const size_t off = (size_t)gr * D + col * 8;
+                k[i] = global_load16(Kh + off);
+                v[i] = global_load16(Vh + off);
+            } else {
+                k[i] = u32x4{0, 0, 0, 0};
+                v[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(FA2_LDS char* Ks, FA2_LDS char* Vs, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = c / kChunksPerRow;
+            const int col = c % kChunksPerRow;
+            lds_store16(Ks + row * (2 * D) + 16 * (col ^ swz_k<D>(row)), k[i]);
+            lds_store16(Vs + row * (2 * D) + 16 * (col ^ swz_v<D>(row)), v[i]);
+        }
+    }
+};
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+void fwd_kernel(const FwdParams p) {
+    constexpr int BC = FwdTile<D>::BC;
+    constexpr int NBS = BC / 32;        // 32-key blocks of S^T per tile
+    constexpr int KSD = D / 16;         // MFMA reduction steps over the head dim
+    constexpr int NBD = D / 32;         // 32-wide blocks of the head dim (O^T)
+    constexpr int KSKV = BC / 16;       // MFMA reduction steps over the keys of a tile
+    constexpr int kTileBytes = BC * D * 2;
+    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kTileBytes];
+    FA2_LDS char* smem = (FA2_LDS char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;     // lane group: which 8 reduction elements this lane holds
+    const int li = lane & 31;    // query row within the wave's 32
+
+    // ---- work item: heaviest causal query tiles first, heads of a level consecutive
+    const int BH = p.B * p.Hq;
+    const int level = blockIdx.x / BH;
+    const int bh = blockIdx.x - level * BH;
+    const int qtile = p.n_qtiles - 1 - level;
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hk = hq / p.G;
+    const int N = p.N;
+
+    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+    const uint16_t* Qh = p.Q + qhead;
+    const uint16_t* Kh = p.K + khead;
+    const uint16_t* Vh = p.V + khead;
+
+    const int q0 = qtile * kFwdRows;
+    const int wq0 = q0 + wave * 32;
+    const int q = wq0 + li;
+    const bool wave_live = wq0 < N;
+
+    // ---- this lane's query row, as 8-element MFMA operands over the head dim
+    bf16x8 qf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 v = {0, 0, 0, 0};
+        if (q < N) v = global_load16(Qh + (size_t)q * D + 16 * ks + 8 * g);
+        qf[ks] = as_bf16x8(v);
+    }
+
+    // ---- key tiles this workgroup visits
+    int n_kv = (N + BC - 1) / BC;
+    if (CAUSAL) {
+        const int last = min(q0 + kFwdRows, N) - 1;
+        n_kv = last / BC + 1;
+    }
+
+    f32x16 o[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) o[i] = zero16();
+    float m_run = kNegInf;   // running max of c * S (log2 domain), same in lanes l and l^32
+    float l_run = 0.f;       // this lane's part of the running row sum
+
+    TileLoader<D, BC> ld;
+    ld.load(Kh, Vh, 0, N, tid);
+    ld.store(smem, smem + kTileBytes, tid);
+    __syncthreads();
+
+    for (int j = 0; j < n_kv; ++j) {
+        const int kv0 = j * BC;
+        FA2_LDS char* Ks = smem + (j & 1) * (2 * kTileBytes);
+        FA2_LDS char* Vs = Ks + kTileBytes;
+        const bool has_next = j + 1 < n_kv;
+        if (has_next) ld.load(Kh, Vh, kv0 + BC, N, tid);
+
+        const bool active = wave_live && !(CAUSAL && kv0 > wq0 + 31);
+        if (active) {
+            // S^T = K Q^T for this tile: NBS blocks of 32 keys x 32 query rows.
+            f32x16 s[NBS];
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs) s[bs] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+#pragma unroll
+                for (int bs = 0; bs < NBS; ++bs) {
+                    const int row = 32 * bs + li;
+                    const int chunk = 2 * ks + g;
+                    const u32x4 a = lds_load16(Ks + row * (2 * D) + 16 * (chunk ^ swz_k<D>(row)));
+                    s[bs] = mfma32(as_bf16x8(a), qf[ks], s[bs]);
+                }
+            }
+
+            // Mask keys above the diagonal and past the end (straddling tiles only).
+            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
+            if (need_mask) {
+#pragma unroll
+                for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
+                    }
+            }
+
+            // Online softmax, log2 domain.
+            float mx = kNegInf;
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
+            mx = max_halves(mx);
+            const float m_new = fmaxf(m_run, mx * p.c);
+            const float alpha = exp2_fast(m_run - m_new);
+            m_run = m_new;
+
+            uint32_t pp[NBS][8];
+            float lsum = 0.f;
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
+                    const float p1 = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
+                    pp[bs][r >> 1] = pack_bf16(p0, p1);
+                    lsum += p0 + p1;
+                }
+            l_run = fmaf(l_run, alpha, lsum);
+
+            // Deferred rescale of the unnormalized accumulator, only if some row's max moved.
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int i = 0; i < NBD; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
+
+            // O^T += V^T P^T.
+            const int j16 = lane & 15;
+            const int half = (lane >> 4) & 1;
+#pragma unroll
+            for (int kk = 0; kk < KSKV; ++kk) {
+                const int bs = kk >> 1, h = kk & 1;
+                const u32x4 pv = {pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2],
+                                  pp[bs][4 * h + 3]};
+                const bf16x8 bfrag = as_bf16x8(pv);
+                const int row1 = 16 * kk + 4 * g + (j16 >> 2);
+                const int row2 = row1 + 8;
+#pragma unroll
+                for (int db = 0; db < NBD; ++db) {
+                    const int col = 32 * db + 16 * half + 4 * (j16 & 3);
+                    const int cchunk = col >> 3, cin = (col & 7) * 2;
+                    const s16x4 t1 = lds_load_tr(Vs + row1 * (2 * D) + 16 * (cchunk ^ swz_v<D>(row1)) + cin);
+                    const s16x4 t2 = lds_load_tr(Vs + row2 * (2 * D) + 16 * (cchunk ^ swz_v<D>(row2)) + cin);
+                    o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
+                }
+            }
+        }
+
+        if (has_next) {
+            FA2_LDS char* Kn = smem + ((j + 1) & 1) * (2 * kTileBytes);
+            ld.store(Kn, Kn + kTileBytes, tid);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O~ / l (one reciprocal per row), L = ln2 * (m + log2 l)
+    if (wave_live) {
+        const float l_tot = sum_halves(l_run);
+        const float inv = 1.0f / l_tot;
+        if (q < N) {
+            uint16_t* Orow = p.O + qhead + (size_t)q * D;
+#pragma unroll
+            for (int db = 0; db < NBD; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * db + 8 * rq + 4 * g;
+                    u32x2 w;
+                    w[0] = pack_bf16(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+                    w[1] = pack_bf16(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
+                }
+            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+    const long grid = (long)p.B * p.Hq * p.n_qtiles;
+    FwdParams arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, CAUSAL>),
+                           dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+    switch (d) {
+        case 64: return causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+        case 128: return causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
+        case 256: return causal ? launch_fwd_t<256, true>(p, stream) : launch_fwd_t<256, false>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa2

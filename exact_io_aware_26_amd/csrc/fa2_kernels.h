@@ -1,0 +1,42 @@
+// fa2_kernels.h -- host-side launch interface between the C ABI and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+struct FwdParams {
+    const uint16_t* Q;  // bf16 [B, Hq, N, D]
+    const uint16_t* K;  // bf16 [B, Hkv, N, D]
+    const uint16_t* V;  // bf16 [B, Hkv, N, D]
+    uint16_t* O;        // bf16 [B, Hq, N, D]
+    float* L;           // fp32 [B, Hq, N]
+    int B, Hq, Hkv, N, G;
+    int n_qtiles;       // ceil(N / rows per workgroup)
+    float c;            // scale * log2(e): scores enter exp2 in the log2 domain
+};
+
+struct BwdParams {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* O;
+    const float* L;
+    const uint16_t* dO;
+    uint16_t* dQ;
+    uint16_t* dK;
+    uint16_t* dV;
+    float* Dsum;   // fp32 [B, Hq, N]     workspace: D = rowsum(dO o O)
+    float* dQacc;  // fp32 [B, Hq, N, D]  workspace: dQ accumulated with atomics
+    int B, Hq, Hkv, N, G;
+    float scale;
+    float c;       // scale * log2(e)
+};
+
+// Rows of Q per forward workgroup (the grid is B * Hq * ceil(N / kFwdRows)).
+constexpr int kFwdRows = 128;
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa2

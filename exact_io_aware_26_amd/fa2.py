@@ -1,0 +1,154 @@
+"""Python binding of libfa2.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in ``include/fa2.h``; this module only checks tensor metadata,
+allocates outputs with PyTorch (device memory and streams are PyTorch's) and
+passes raw pointers.  There is no fallback: if ``libfa2.so`` is missing the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+FA2_OK = 0
+FA2_ERR_INVALID_ARGUMENT = 1
+FA2_ERR_UNSUPPORTED = 2
+FA2_ERR_HIP = 3
+
+EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_validate_fwd",
+           "fa2_validate_bwd", "fa2_status_string", "fa2_last_error")
+
+_lib = None
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {detail}")
+
+
+def load(path: str | None = None):
+    """Load libfa2.so (built in-tree by ``exact_io_aware_26_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_26_amd.build` "
+                           "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd.restype = i
+    lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa2_bwd.restype = i
+    lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa2_bwd_workspace_bytes.restype = sz
+    lib.fa2_validate_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
+    lib.fa2_validate_fwd.restype = i
+    lib.fa2_validate_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f]
+    lib.fa2_validate_bwd.restype = i
+    lib.fa2_status_string.argtypes = [i]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_last_error.argtypes = []
+    lib.fa2_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa2_status_string(status).decode()
+
+
+def _check(status: int, lib) -> None:
+    if status != FA2_OK:
+        raise FA2Error(status, lib.fa2_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, Hq, k.shape[1], N, d
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            scale: float | None = None, out: torch.Tensor | None = None,
+            lse: torch.Tensor | None = None):
+    """O = softmax(scale * q k^T [+ causal mask]) v and L (natural-log logsumexp per row).
+
+    q [B,Hq,N,d], k/v [B,Hkv,N,d] contiguous bf16 GPU tensors.  Returns
+    (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32).  scale defaults to 1/sqrt(d).
+    """
+    lib = load()
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = lib.fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                     int(bool(causal)), float(scale), _stream_handle(q))
+    _check(st, lib)
+    return out, lse
+
+
+def workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return load().fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, do: torch.Tensor, causal: bool = False,
+             scale: float | None = None, workspace: torch.Tensor | None = None):
+    """dQ, dK, dV of sum(do * o) for the forward above (P rebuilt from lse).
+
+    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) bf16.  A caller
+    may pass a reusable uint8 ``workspace`` of at least
+    ``workspace_bytes(...)`` bytes (256-byte aligned).
+    """
+    lib = load()
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    for name, t in (("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    st = lib.fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                     _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d,
+                     int(bool(causal)), float(scale), _stream_handle(q))
+    _check(st, lib)
+    return dq, dk, dv

@@ -1,0 +1,138 @@
+/*
+ * fa2.h -- C ABI of the gfx950 (MI355X) exact-attention library libfa2.so.
+ *
+ * The library computes exact attention the FlashAttention-2 way: the forward
+ * pass tiles the query rows across workgroups, streams K/V tiles through LDS
+ * and keeps an online softmax with a deferred rescale of an unnormalized fp32
+ * accumulator, emitting the per-row logsumexp L = m + log(l); the backward
+ * pass rebuilds P = exp(S - L) from L and produces dQ, dK, dV, looping over
+ * K/V tiles on the outside and accumulating dQ in fp32 with atomics.
+ * (FlashAttention-2 summary page, zhaifeiyue.github.io: section 2 "Q2
+ * method" -- deferred rescaling, logsumexp, sequence parallelism, split-Q;
+ * section 3 "Target operation" -- O = softmax(QK^T)V, optional causal mask,
+ * FP16/BF16 inputs with an FP32 accumulator; section 4 symbol table -- L and
+ * D = rowsum(dO o O); section 4 checks -- GQA/MQA by shared K/V heads with
+ * dK/dV summed over the sharing heads; section 7 -- dQ accumulated with
+ * atomic adds.  Head dimensions up to 256 and MQA/GQA: ai.oldpan.me, "New
+ * features".)
+ *
+ * Definition computed, per batch b and query head hq, with key/value head
+ * hk = hq / (Hq / Hkv):
+ *     S = scale * Q K^T,   S_ij = -inf for j > i when causal,
+ *     L_i = ln sum_j exp(S_ij),   P = exp(S - L),   O = P V,
+ *     dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q   (dK, dV summed over the
+ *     query heads that share a key/value head).
+ *
+ * Data layout (all tensors contiguous, row-major, device memory):
+ *     Q, O, dO, dQ : bf16 [B, Hq,  N, d]     (bf16 = raw 16-bit storage)
+ *     K, V, dK, dV : bf16 [B, Hkv, N, d]
+ *     L            : fp32 [B, Hq,  N]        natural-log logsumexp of the
+ *                                             scaled, masked scores
+ * Every device pointer must be 16-byte aligned.  Query and key sequence
+ * lengths are equal (N).  d must be 64, 128 or 256.  Hq must be a multiple
+ * of Hkv.  scale must be finite and > 0 (typically 1/sqrt(d)).  Rounding to
+ * bf16 is round-to-nearest-even.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer
+ * after a call returns and allocates no device memory.  Outputs are fully
+ * overwritten (no zeroing needed).  Inputs are never written.  An output may
+ * not alias an input.
+ *
+ * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream).  Calls are asynchronous: argument errors are reported
+ * before anything is launched (nothing is written then); a launch failure
+ * returns FA2_ERR_HIP; a fault inside a kernel surfaces at the caller's next
+ * synchronization with the stream, not as a return value.  The library is
+ * thread-safe (no mutable global state beyond a per-thread error message).
+ *
+ * Determinism: the forward pass is bitwise reproducible.  The backward
+ * pass's dQ is summed with fp32 atomics and is reproducible only up to the
+ * order of those additions; dK and dV are reproducible.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa2_status {
+    FA2_OK = 0,
+    FA2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned/aliased pointer, bad size or scale */
+    FA2_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement (d) */
+    FA2_ERR_HIP = 3               /* the HIP runtime rejected a launch */
+} fa2_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and L.
+ *   Q [B,Hq,N,d], K/V [B,Hkv,N,d] bf16 inputs; O [B,Hq,N,d] bf16 and
+ *   L [B,Hq,N] fp32 outputs.  causal != 0 masks keys j > i.
+ * Any of B, Hq, N equal to 0 is an empty problem: FA2_OK, nothing launched
+ * (pointers may then be NULL).
+ * Errors: FA2_ERR_INVALID_ARGUMENT for a negative size, Hkv < 1 with work,
+ * Hq % Hkv != 0, a NULL or non-16-byte-aligned pointer, O or L aliasing an
+ * input, O aliasing L, a non-finite or non-positive scale, or sizes whose
+ * element counts overflow 64 bits; FA2_ERR_UNSUPPORTED for d not in
+ * {64, 128, 256}; FA2_ERR_HIP if the launch fails.
+ */
+fa2_status fa2_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void *stream);
+
+/*
+ * Bytes of device workspace fa2_bwd needs: an fp32 [B,Hq,N] array for
+ * D = rowsum(dO o O) and an fp32 [B,Hq,N,d] array accumulating dQ, each
+ * starting on a 256-byte boundary.  Returns 0 for an empty problem and for
+ * invalid sizes (negative, or Hq % Hkv != 0).
+ */
+size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Backward pass: dQ, dK, dV of sum(dO o O) for the forward defined above.
+ *   Q, K, V: the forward's inputs; O [B,Hq,N,d] bf16 and L [B,Hq,N] fp32:
+ *   the forward's outputs (P is rebuilt from L); dO [B,Hq,N,d] bf16.
+ *   dQ [B,Hq,N,d], dK and dV [B,Hkv,N,d]: bf16 outputs (for GQA, dK/dV are
+ *   summed over the Hq/Hkv query heads sharing each key/value head).
+ *   workspace: caller-allocated device memory, 256-byte aligned, of at least
+ *   fa2_bwd_workspace_bytes(...) bytes; contents undefined on entry and exit.
+ * Errors: as fa2_fwd, plus FA2_ERR_INVALID_ARGUMENT when the workspace is
+ * NULL, misaligned or too small, or when an output aliases an input or
+ * another output.
+ */
+fa2_status fa2_bwd(const void *Q, const void *K, const void *V, const void *O,
+                   const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                   void *workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void *stream);
+
+/*
+ * The argument checks of fa2_fwd / fa2_bwd alone: no HIP call is made, so
+ * they run without a GPU.  Same return codes as the full calls.
+ */
+fa2_status fa2_validate_fwd(const void *Q, const void *K, const void *V, const void *O,
+                            const float *L, int B, int Hq, int Hkv, int N, int d,
+                            int causal, float scale);
+fa2_status fa2_validate_bwd(const void *Q, const void *K, const void *V, const void *O,
+                            const float *L, const void *dO, const void *dQ,
+                            const void *dK, const void *dV, const void *workspace,
+                            size_t workspace_bytes, int B, int Hq, int Hkv, int N,
+                            int d, int causal, float scale);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *fa2_status_string(fa2_status s);
+
+/*
+ * Detail of the last non-OK status returned on the calling thread (which
+ * check failed, or the HIP error string); "" if none.  Valid until the next
+ * call on the same thread.
+ */
+const char *fa2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */
