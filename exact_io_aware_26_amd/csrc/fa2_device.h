@@ -25,6 +25,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA2_LDS __attribute__((address_space(3)))
 
+// Bit reinterpretation through by-value parameters.  Never apply
+// __builtin_bit_cast directly to an element of an ext_vector_type value
+// (`v[i]`): this compiler then reads element 0 whatever i is.
+__device__ __forceinline__ float u32_as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t f32_as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -53,14 +59,16 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
 // Combine lane l with lane l ^ 32 (v_permlane32_swap of a register with itself
 // yields {low half, low half} and {high half, high half}).
 __device__ __forceinline__ float max_halves(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t u = f32_as_u32(x);
     auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1]));
+    const uint32_t lo = pr[0], hi = pr[1];
+    return fmaxf(u32_as_f32(lo), u32_as_f32(hi));
 }
 __device__ __forceinline__ float sum_halves(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t u = f32_as_u32(x);
     auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
+    const uint32_t lo = pr[0], hi = pr[1];
+    return u32_as_f32(lo) + u32_as_f32(hi);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -316,6 +316,204 @@ int oracle_bwd_head(const double *Q, const double *K, const double *V,
     return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * The same definition evaluated at the method's working precision.
+ *
+ * The method multiplies FP16/BF16 operands with FP32 accumulation (summary
+ * page, section 3 "Target operation"); its outputs are stored in bf16.  So
+ * the probabilities P enter both P V (forward) and P^T dO (backward) as
+ * bf16, dS enters dS^T Q and dS K as bf16, and D = rowsum(dO o O) is formed
+ * from the stored bf16 O.  This variant rounds exactly there (values first
+ * rounded to fp32, then to bf16, round to nearest even) and keeps every
+ * other step of the definition in double:
+ *   forward:  p_ij = exp(S_ij - m_i) in [0, 1];  O_i = sum_j bf16(p_ij) V_j
+ *             / sum_j p_ij;  O is stored as bf16(O).
+ *   backward: D_i = dO_i . bf16(O_i);  P_ij = exp(S_ij - L_i);
+ *             dV_j = sum_i bf16(P_ij) dO_i;  dS_ij = P_ij (dP_ij - D_i);
+ *             dQ_i = scale sum_j bf16(dS_ij) K_j;  dK_j = scale sum_i bf16(dS_ij) Q_i.
+ * The gradients are returned unrounded (double).  It measures how far an
+ * exact execution of the method at this precision lands from the exact
+ * function; the tests use it to calibrate, never to replace, the reference.
+ * ------------------------------------------------------------------------ */
+static double round_bf16(double x)
+{
+    float f = (float)x;
+    unsigned int u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (double)f;   /* inf / nan */
+    u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Forward row at the working precision: O_i (unrounded) from bf16(p_ij), and L_i. */
+static double row_forward_bf16(const double *Qh, const double *Kh, const double *Vh,
+                               int N, int d, double scale, int causal, int i,
+                               double *s, double *o)
+{
+    const double *q = Qh + (size_t)i * d;
+    double m = -INFINITY;
+    for (int j = 0; j < N; ++j) {
+        s[j] = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int t = 0; t < d; ++t) o[t] = 0.0;
+    for (int j = 0; j < N; ++j) {
+        double p = exp(s[j] - m);
+        l += p;
+        if (p == 0.0) continue;
+        double pb = round_bf16(p);
+        const double *v = Vh + (size_t)j * d;
+        for (int t = 0; t < d; ++t) o[t] += pb * v[t];
+    }
+    for (int t = 0; t < d; ++t) o[t] /= l;
+    return m + log(l);
+}
+
+int oracle_fwd_bf16(const double *Q, const double *K, const double *V, double *O,
+                    double *L, int B, int Hq, int Hkv, int N, int d, int causal,
+                    double scale)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if ((long)B * Hq * N == 0) return 0;
+    const int G = Hq / Hkv;
+    const long rows = (long)B * Hq * N;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(dynamic, 16)
+        for (long r = 0; r < rows; ++r) {
+            int i = (int)(r % N);
+            int hq = (int)((r / N) % Hq);
+            int b = (int)(r / ((long)N * Hq));
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);
+            const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);
+            double l = row_forward_bf16(Qh, Kh, Vh, N, d, scale, causal, i, s, O + (size_t)r * d);
+            if (L) L[r] = l;
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/* Working-precision backward of one key/value head (b, hk): dQg [G,N,d] of
+ * query heads hk*G.., dKh and dVh [N,d]. */
+static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double *V,
+                                 const double *dO, int Hq, int Hkv, int N, int d,
+                                 int causal, double scale, int b, int hk,
+                                 double *dQg, double *dKh, double *dVh, double *Dg)
+{
+    const int G = Hq / Hkv;
+    const double *Kh = head_ptr(K, b, hk, Hkv, N, d);
+    const double *Vh = head_ptr(V, b, hk, Hkv, N, d);
+    double *Lst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    double *Dst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    /* L_i and D_i = dO_i . bf16(O_i), with O_i from the working-precision forward. */
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 8)
+        for (long r = 0; r < (long)G * N; ++r) {
+            int g = (int)(r / N), i = (int)(r % N);
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+            Lst[r] = row_forward_bf16(Qh, Kh, Vh, N, d, scale, causal, i, s, o);
+            double D = 0.0;
+            for (int t = 0; t < d; ++t) D += dOr[t] * round_bf16(o[t]);
+            Dst[r] = D;
+        }
+        free(s);
+        free(o);
+    }
+    /* dQ_i = scale * sum_j bf16(dS_ij) K_j */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (long r = 0; r < (long)G * N; ++r) {
+        int g = (int)(r / N), i = (int)(r % N);
+        int hq = hk * G + g;
+        const double *q = head_ptr(Q, b, hq, Hq, N, d) + (size_t)i * d;
+        const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+        double *dq = dQg + (size_t)r * d;
+        for (int t = 0; t < d; ++t) dq[t] = 0.0;
+        for (int j = 0; j < N; ++j) {
+            double p = exp(score(q, Kh + (size_t)j * d, d, scale, causal, i, j) - Lst[r]);
+            if (p == 0.0) continue;
+            const double *v = Vh + (size_t)j * d;
+            double dp = 0.0;
+            for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+            double ds = round_bf16(p * (dp - Dst[r]));
+            const double *k = Kh + (size_t)j * d;
+            for (int t = 0; t < d; ++t) dq[t] += ds * k[t];
+        }
+        for (int t = 0; t < d; ++t) dq[t] *= scale;
+    }
+    /* dV_j = sum bf16(P_ij) dO_i ;  dK_j = scale * sum bf16(dS_ij) Q_i */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int j = 0; j < N; ++j) {
+        const double *k = Kh + (size_t)j * d;
+        const double *v = Vh + (size_t)j * d;
+        double *dk = dKh + (size_t)j * d;
+        double *dv = dVh + (size_t)j * d;
+        for (int t = 0; t < d; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
+        for (int g = 0; g < G; ++g) {
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
+            for (int i = 0; i < N; ++i) {
+                const double *q = Qh + (size_t)i * d;
+                double p = exp(score(q, k, d, scale, causal, i, j) - Lst[(long)g * N + i]);
+                if (p == 0.0) continue;
+                const double *dOr = dOh + (size_t)i * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                double pb = round_bf16(p);
+                double ds = round_bf16(p * (dp - Dst[(long)g * N + i]));
+                for (int t = 0; t < d; ++t) {
+                    dv[t] += pb * dOr[t];
+                    dk[t] += ds * q[t];
+                }
+            }
+        }
+        for (int t = 0; t < d; ++t) dk[t] *= scale;
+    }
+    if (Dg) memcpy(Dg, Dst, sizeof(double) * (size_t)G * N);
+    free(Lst);
+    free(Dst);
+}
+
+int oracle_bwd_bf16(const double *Q, const double *K, const double *V,
+                    const double *dO, double *dQ, double *dK, double *dV, double *D,
+                    int B, int Hq, int Hkv, int N, int d, int causal, double scale)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if ((long)B * Hq * N == 0) return 0;
+    const int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b)
+        for (int hk = 0; hk < Hkv; ++hk) {
+            size_t qoff = (((size_t)b * Hq + (size_t)hk * G) * N) * d;
+            size_t koff = (((size_t)b * Hkv + hk) * (size_t)N) * d;
+            double *Dg = D ? D + ((size_t)b * Hq + (size_t)hk * G) * N : NULL;
+            bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+                                 dQ + qoff, dK + koff, dV + koff, Dg);
+        }
+    return 0;
+}
+
+int oracle_bwd_bf16_head(const double *Q, const double *K, const double *V,
+                         const double *dO, int B, int Hq, int Hkv, int N, int d,
+                         int causal, double scale, int b, int hk, double *dQg,
+                         double *dKh, double *dVh)
+{
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if (b < 0 || b >= B || hk < 0 || hk >= Hkv) return -1;
+    if (N == 0) return 0;
+    bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk, dQg, dKh, dVh, NULL);
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -48,7 +48,13 @@ def _open(path: str):
                                ctypes.c_double]
     lib.oracle_bwd_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double,
                                     i, i, dp, dp, dp, dp, dp]
-    for f in (lib.oracle_fwd, lib.oracle_fwd_rows, lib.oracle_bwd, lib.oracle_bwd_head):
+    lib.oracle_fwd_bf16.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_bwd_bf16.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i,
+                                    ctypes.c_double]
+    lib.oracle_bwd_bf16_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double,
+                                         i, i, dp, dp, dp]
+    for f in (lib.oracle_fwd, lib.oracle_fwd_rows, lib.oracle_bwd, lib.oracle_bwd_head,
+              lib.oracle_fwd_bf16, lib.oracle_bwd_bf16, lib.oracle_bwd_bf16_head):
         f.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -180,3 +186,58 @@ def backward_head(q, k, v, do, b: int, hk: int, causal: bool = False,
     if rc != 0:
         raise ValueError("oracle_bwd_head: bad sizes or head index")
     return dq, dk, dv, L, D
+
+
+def forward_bf16(q, k, v, causal: bool = False, scale: float | None = None, lib=None):
+    """The forward at the method's working precision (bf16 P in P V): (O unrounded, L)."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    if scale is None:
+        scale = default_scale(d)
+    o = np.empty_like(q)
+    L = np.empty((B, Hq, N), dtype=np.float64)
+    rc = lib.oracle_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
+                             B, Hq, Hkv, N, d, int(causal), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_fwd_bf16: bad sizes")
+    return o, L
+
+
+def backward_bf16(q, k, v, do, causal: bool = False, scale: float | None = None, lib=None,
+                  return_d: bool = False):
+    """The backward at the method's working precision: (dQ, dK, dV) unrounded (and D)."""
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    D = np.empty((B, Hq, N), dtype=np.float64)
+    rc = lib.oracle_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(D), B, Hq, Hkv, N, d, int(causal), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_bwd_bf16: bad sizes")
+    return (dq, dk, dv, D) if return_d else (dq, dk, dv)
+
+
+def backward_bf16_head(q, k, v, do, b: int, hk: int, causal: bool = False,
+                       scale: float | None = None, lib=None):
+    """Working-precision backward of key/value head (b, hk): (dQ [G,N,d], dK [N,d], dV [N,d])."""
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.empty((G, N, d), dtype=np.float64)
+    dk = np.empty((N, d), dtype=np.float64)
+    dv = np.empty((N, d), dtype=np.float64)
+    rc = lib.oracle_bwd_bf16_head(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, Hq, Hkv, N, d,
+                                  int(causal), float(scale), int(b), int(hk), _ptr(dq),
+                                  _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_bwd_bf16_head: bad sizes or head index")
+    return dq, dk, dv

@@ -315,6 +315,76 @@ def pin_sampled_entry_points(lib):
         _close(hD, D[1, 2:4], 0, "backward_head D")
 
 
+# ----------------------------------------------------------------------------
+# 6. the working-precision variant (bf16 P, O and dS at the method's rounding points)
+# ----------------------------------------------------------------------------
+U_BF16 = 2.0 ** -8 + 2.0 ** -23     # RNE to 8 significant bits, after a first rounding to fp32
+
+
+def pin_working_precision(lib):
+    # The two-key example (hand-derived working-precision values in the golden file):
+    # the forward rounds the unnormalized exp(S - rowmax) = 1/3 of row 1; every
+    # backward rounding point holds a bf16-exact value.
+    with open(os.path.join(GOLDEN, "two_key_example.json")) as f:
+        g = json.load(f)
+    q = np.array(_golden_value(g["Q"])).reshape(1, 1, 2, 1)
+    k = np.array(_golden_value(g["K"])).reshape(1, 1, 2, 1)
+    v = np.array(_golden_value(g["V"])).reshape(1, 1, 2, 1)
+    do = np.array(_golden_value(g["dO"])).reshape(1, 1, 2, 1)
+    for causal, key in ((False, "noncausal"), (True, "causal")):
+        exp = {n: np.array(_golden_value(val)) for n, val in g[key].items()}
+        o, L = orc.forward_bf16(q, k, v, causal, g["scale"], lib=lib)
+        wp = np.array([[float(eval(str(x), {"__builtins__": {}})) for x in r]
+                       for r in g["working_precision"][key]["O"]])
+        _close(o.reshape(2, 1), wp, 1e-14, f"bf16 golden {key} O")
+        _close(L.reshape(2), exp["L"], 1e-14, f"bf16 golden {key} L")
+        dq, dk, dv = orc.backward_bf16(q, k, v, do, causal, g["scale"], lib=lib)
+        _close(dq.reshape(2, 1), exp["dQ"], 1e-14, f"bf16 golden {key} dQ")
+        _close(dk.reshape(2, 1), exp["dK"], 1e-14, f"bf16 golden {key} dK")
+        _close(dv.reshape(2, 1), exp["dV"], 1e-14, f"bf16 golden {key} dV")
+    # Rigorous first-order bounds of the roundings, which must also be approached
+    # (so the rounding really happens, to 8 significant bits).
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, N, d = 1, 2, 1, 60, 8
+    q, k, v = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    do = _rand(rng, B, Hq, N, d)
+    scale = 0.9
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    for causal in (False, True):
+        s = scale * np.einsum("bhid,bhjd->bhij", q, kr)
+        if causal:
+            s = np.where(np.triu(np.ones((N, N), bool), 1), -np.inf, s)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        l = p.sum(-1, keepdims=True)
+        o_ex, L_ex = orc.forward(q, k, v, causal, scale, lib=lib)
+        o_b, L_b = orc.forward_bf16(q, k, v, causal, scale, lib=lib)
+        _close(L_b, L_ex, 1e-13, "bf16 forward L is unrounded")
+        bound = U_BF16 * np.einsum("bhij,bhjd->bhid", p, np.abs(vr)) / l
+        ratio = np.abs(o_b - o_ex) / np.maximum(bound, 1e-300)
+        assert ratio.max() <= 1.0 + 1e-9, f"forward rounding above its bound: {ratio.max()}"
+        assert ratio.max() >= 0.25, f"forward rounding far below its bound: {ratio.max()}"
+        P = np.exp(s - L_ex[..., None])
+        _, _, dv_ex, _ = orc.backward(q, k, v, do, causal, scale, lib=lib)
+        _, _, dv_b = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib)
+        bound = U_BF16 * np.einsum("bhij,bhid->bhjd", P, np.abs(do)).reshape(B, Hkv, 2, N, d).sum(2)
+        ratio = np.abs(dv_b - dv_ex) / np.maximum(bound, 1e-300)
+        assert ratio.max() <= 1.0 + 1e-9, f"dV rounding above its bound: {ratio.max()}"
+        assert ratio.max() >= 0.25, f"dV rounding far below its bound: {ratio.max()}"
+        # D is formed from the stored (bf16) O of the working-precision forward.
+        _, _, _, D_b = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib, return_d=True)
+        o_stored = o_b.astype(np.float32).view(np.uint32).astype(np.uint64)
+        o_stored = (((o_stored + 0x7FFF + ((o_stored >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+        o_stored = o_stored.view(np.float32).astype(np.float64)
+        _close(D_b, np.sum(do * o_stored, axis=-1), 1e-13, "bf16 D from the stored O")
+        assert np.max(np.abs(D_b - np.sum(do * o_b, axis=-1))) > 1e-6, "D ignores the O rounding"
+        # The one-head entry point agrees with the full one.
+        dq_b, dk_b, dv_b2 = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib)
+        hq_, hk_, hv_ = orc.backward_bf16_head(q, k, v, do, 0, 0, causal, scale, lib=lib)
+        _close(hq_, dq_b[0], 0, "bf16 head dQ")
+        _close(hk_, dk_b[0, 0], 0, "bf16 head dK")
+        _close(hv_, dv_b2[0, 0], 0, "bf16 head dV")
+
+
 ALL_PINS = [pin_golden_two_key, pin_torch_forward, pin_torch_backward,
             pin_finite_differences, pin_closed_forms, pin_invariants,
-            pin_sampled_entry_points]
+            pin_sampled_entry_points, pin_working_precision]

@@ -22,21 +22,31 @@ MUTATIONS = [
     ("log2 instead of natural log in L", "return m + log(sum);", "return m + log2(sum);"),
     ("row maximum not subtracted inside the sum", "sum += exp(s[j] - m);", "sum += exp(s[j]);"),
     ("wrong GQA head mapping in the forward",
-     "const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);",
-     "const double *Kh = head_ptr(K, b, hq % Hkv, Hkv, N, d);"),
+     "const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);\n            const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);\n            double *o = O",
+     "const double *Kh = head_ptr(K, b, hq % Hkv, Hkv, N, d);\n            const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);\n            double *o = O"),
     ("value row index i instead of j", "const double *v = Vh + (size_t)j * d;\n        for (int t = 0; t < d; ++t) o[t] += p * v[t];",
      "const double *v = Vh + (size_t)i * d;\n        for (int t = 0; t < d; ++t) o[t] += p * v[t];"),
     ("D dropped from dS in dQ", "double ds = p * (dp - Dst[r]);", "double ds = p * dp;"),
     ("wrong sign of dS in dK", "double ds = p * (dp - Dst[(long)g * N + i]);",
      "double ds = p * (Dst[(long)g * N + i] - dp);"),
     ("D without the P weight", "D += p * dp;", "D += dp;"),
-    ("dQ built from Q instead of K", "for (int t = 0; t < d; ++t) dq[t] += ds * k[t];",
-     "for (int t = 0; t < d; ++t) dq[t] += ds * q[t];"),
-    ("scale missing from dK", "for (int t = 0; t < d; ++t) dk[t] *= scale;", ""),
+    ("dQ built from Q instead of K",
+     "double ds = p * (dp - Dst[r]);\n                const double *k = Kh + (size_t)j * d;\n                for (int t = 0; t < d; ++t) dq[t] += ds * k[t];",
+     "double ds = p * (dp - Dst[r]);\n                const double *k = Kh + (size_t)j * d;\n                for (int t = 0; t < d; ++t) dq[t] += ds * q[t];"),
+    ("scale missing from dK", "for (int t = 0; t < d; ++t) dk[t] *= scale;\n    }\n\n    if (Lg)",
+     "\n    }\n\n    if (Lg)"),
     ("dV uses the key-side row of dO (transposed operand)", "dv[t] += p * dOr[t];",
      "dv[t] += p * dOh[(size_t)j * d + t];"),
-    ("dK sums over one query head of the group only", "for (int g = 0; g < G; ++g) {",
-     "for (int g = 0; g < 1; ++g) {"),
+    ("dK sums over one query head of the group only",
+     "for (int g = 0; g < G; ++g) {\n            int hq = hk * G + g;\n            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);\n            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);\n            for (int i = 0; i < N; ++i) {\n                const double *q = Qh + (size_t)i * d;\n                double sij",
+     "for (int g = 0; g < 1; ++g) {\n            int hq = hk * G + g;\n            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);\n            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);\n            for (int i = 0; i < N; ++i) {\n                const double *q = Qh + (size_t)i * d;\n                double sij"),
+    ("bf16 rounding to 7 significant bits", "u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;",
+     "u = (u + 0xffffu + ((u >> 17) & 1u)) & 0xfffe0000u;"),
+    ("bf16 rounding dropped from P of the working-precision forward", "double pb = round_bf16(p);\n        const double *v",
+     "double pb = p;\n        const double *v"),
+    ("bf16 rounding dropped from P of the working-precision dV", "double pb = round_bf16(p);\n                double ds",
+     "double pb = p;\n                double ds"),
+    ("working-precision D from the unrounded O", "D += dOr[t] * round_bf16(o[t]);", "D += dOr[t] * o[t];"),
 ]
 
 
