@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path once: the forward pass (O, L) and the backward pass
+(D, the K/V-tile loop with dQ atomics, the dQ conversion) of causal bf16
+attention, B=4, H=16, N=8192, d=128, on seeded synthetic N(0,1) inputs that
+are resident in HBM before timing starts.
+
+FLOPs follow the FlashAttention-2 convention (summary page, section 3
+"FLOPs"): forward 4*B*H*N^2*d, halved with the causal mask; backward 2.5x
+the forward.  Peak: MI355X dense bf16 matrix-core rate, 256 CUs x 2.4 GHz x
+4096 FLOP/clk = 2516.6 TFLOP/s.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s fwd & bwd (bf16, d=128, causal) and % of MI355X MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_26_amd", "csrc", f)
+                  for f in ("fa2_bwd.hip", "fa2_device.h", "fa2_kernels.h")]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(launches_per_dispatch: float = 1.0):
+    """HBM bytes per launch of the backward main kernel from committed rocprofv3
+    counter runs, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_digest():
+        return None
+    return float(t["bytes_per_launch"]) * launches_per_dispatch
+
+
+def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
+    """The fp64 oracle on whole (batch, head) slices of the same inputs until ~budget_s."""
+    import numpy as np
+    from exact_io_aware_26_amd import inputs
+    from oracle import oracle as orc
+
+    lib = orc.load()
+    G = w.Hq // w.Hkv
+    heads, flops, t_total = 0, 0.0, 0.0
+    per_head_flops = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.Hq)
+    while heads < w.B * w.Hq:
+        b, hq = divmod(heads, w.Hq)
+        hk = hq // G
+        q = inputs.bf16_bits_to_f64(qb[b:b + 1, hq:hq + 1])
+        k = inputs.bf16_bits_to_f64(kb[b:b + 1, hk:hk + 1])
+        v = inputs.bf16_bits_to_f64(vb[b:b + 1, hk:hk + 1])
+        do = inputs.bf16_bits_to_f64(dob[b:b + 1, hq:hq + 1])
+        t0 = time.perf_counter()
+        orc.forward(q, k, v, w.causal, w.scale, lib=lib)
+        orc.backward(q, k, v, do, w.causal, w.scale, lib=lib)
+        t_total += time.perf_counter() - t0
+        flops += per_head_flops
+        heads += 1
+        log(f"cpu baseline: {heads} head(s) in {t_total:.1f} s")
+        if t_total >= budget_s:
+            break
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.num_threads(lib),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle forward+backward of {heads} whole (batch, head) slice(s) "
+                   f"[1,1,{w.N},{w.d}] causal of the same inputs, {t_total:.1f} s; "
+                   "rate = the slices' FLOPs (same convention) / wall time"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 to skip)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence forward figure")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path, so --gpus {args.gpus} "
+              "is not supported; run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_io_aware_26_amd import fa2, inputs, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    fa2.load()
+    dev = torch.device("cuda:0")
+    w = workloads.BWD
+    log(f"workload {w.name}: generating seeded inputs")
+    qb, kb, vb, dob = inputs.attention_inputs(w.seed, w.B, w.Hq, w.Hkv, w.N, w.d, with_grad=True)
+
+    def to_dev(x):
+        return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (to_dev(x) for x in (qb, kb, vb, dob))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa2.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
+    grads = (dq, dk, dv)
+
+    def fwd():
+        fa2.forward(q, k, v, causal=w.causal, out=o, lse=lse)
+
+    def bwd(stages):
+        fa2.backward(q, k, v, o, lse, do, causal=w.causal, workspace=ws, grads=grads, stages=stages)
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        fwd()
+        bwd(fa2.BWD_ALL)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} step(s)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        fwd()
+        e[1].record()
+        bwd(fa2.BWD_PREPROCESS)
+        e[2].record()
+        bwd(fa2.BWD_MAIN)
+        e[3].record()
+        bwd(fa2.BWD_FINALIZE)
+        e[4].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+
+    def avg(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in ev) / args.steps
+
+    fwd_ms, pre_ms, main_ms, fin_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    bwd_ms = pre_ms + main_ms + fin_ms
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms: fwd {fwd_ms:.3f} ms, bwd pre {pre_ms:.3f} + main {main_ms:.3f} "
+        f"+ convert {fin_ms:.3f} ms")
+
+    main_tflops = bwd_f / (main_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    roofline = {
+        "kernel": "bwd_main_kernel<128, causal> (backward K/V-tile loop)",
+        "bound": "mfma",
+        "achieved": main_tflops,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": main_tflops / PEAK_BF16_TFLOPS,
+        "traffic": traffic,
+        "avg_launch_ms": main_ms,
+        "algorithmic_flops_per_launch": bwd_f,
+    }
+
+    extra = {}
+    if not args.no_extra:
+        wl = workloads.LONG
+        log(f"extra forward figure: {wl.name}")
+        g = torch.Generator(device=dev).manual_seed(wl.seed)
+        ql = torch.randn(wl.B, wl.Hq, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+        kl = torch.randn(wl.B, wl.Hkv, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+        vl = torch.randn(wl.B, wl.Hkv, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+        ol, ll = fa2.forward(ql, kl, vl, causal=wl.causal)
+        for _ in range(3):
+            fa2.forward(ql, kl, vl, causal=wl.causal, out=ol, lse=ll)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fa2.forward(ql, kl, vl, causal=wl.causal, out=ol, lse=ll)
+        e1.record()
+        torch.cuda.synchronize()
+        lms = e0.elapsed_time(e1) / 10
+        extra[wl.name] = {"fwd_ms": lms, "fwd_tflops": wl.fwd_flops() / (lms * 1e-3) / 1e12,
+                          "fwd_pct_peak": 100 * wl.fwd_flops() / (lms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del ql, kl, vl, ol, ll
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, qb, kb, vb, dob, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed},
+        "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_ms,
+        "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
+        "bwd_ms": bwd_ms,
+        "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
+        "bwd_stage_ms": {"preprocess": pre_ms, "main": main_ms, "finalize": fin_ms},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

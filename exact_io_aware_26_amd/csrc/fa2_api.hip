@@ -230,7 +230,17 @@ fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, c
                    const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
                    float scale, void* stream) {
+    return fa2_bwd_stages(FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
+                          B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const void* V,
+                          const void* O, const float* L, const void* dO, void* dQ, void* dK,
+                          void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
+                          int Hkv, int N, int d, int causal, float scale, void* stream) {
     g_last_error[0] = '\0';
+    if (stages == 0 || (stages & ~FA2_BWD_ALL) != 0)
+        return fail(FA2_ERR_INVALID_ARGUMENT, "stage mask must be a non-empty subset of FA2_BWD_ALL");
     bool empty;
     Sizes sz;
     fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
@@ -256,7 +266,7 @@ fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, c
     p.G = Hq / Hkv;
     p.scale = scale;
     p.c = (float)((double)scale * kLog2e);
-    hipError_t e = fa2::launch_bwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    hipError_t e = fa2::launch_bwd(p, d, causal != 0, stages, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
     return FA2_OK;
 }

@@ -416,10 +416,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const BwdParams p, 
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream) {
     BwdParams arg = p;
     const long rows = (long)p.B * p.Hq * p.N;
-    {
+    if (stages & 1u) {
         constexpr int RPB = 256 / (D / 8);
         long rows_arg = rows;
         void* args[] = {&arg, &rows_arg};
@@ -427,7 +427,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                                        dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
-    {
+    if (stages & 2u) {
         constexpr int BC = BwdCfg<D>::BC;
         const long grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
         void* args[] = {&arg};
@@ -435,21 +435,22 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                                        dim3((unsigned)grid), dim3(64 * BwdCfg<D>::NW), args, 0, stream);
         if (e != hipSuccess) return e;
     }
-    {
+    if (stages & 4u) {
         long n8 = rows * D / 8;
         void* args[] = {&arg, &n8};
         return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_convert_kernel),
                                dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
     }
+    return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream) {
     switch (d) {
-        case 64: return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
-        case 128: return causal ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
-        case 256: return causal ? launch_bwd_t<256, true>(p, stream) : launch_bwd_t<256, false>(p, stream);
+        case 64: return causal ? launch_bwd_t<64, true>(p, stages, stream) : launch_bwd_t<64, false>(p, stages, stream);
+        case 128: return causal ? launch_bwd_t<128, true>(p, stages, stream) : launch_bwd_t<128, false>(p, stages, stream);
+        case 256: return causal ? launch_bwd_t<256, true>(p, stages, stream) : launch_bwd_t<256, false>(p, stages, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,6 +37,7 @@ struct BwdParams {
 constexpr int kFwdRows = 128;
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+// stages: bit 0 preprocess (D, zero the dQ accumulator), bit 1 main loop, bit 2 dQ convert.
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream);
 
 }  // namespace fa2

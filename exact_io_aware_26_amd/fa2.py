@@ -22,8 +22,10 @@ FA2_ERR_INVALID_ARGUMENT = 1
 FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
-EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_validate_fwd",
-           "fa2_validate_bwd", "fa2_status_string", "fa2_last_error")
+EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_bwd_workspace_bytes",
+           "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string", "fa2_last_error")
+
+BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL = 1, 2, 4, 7
 
 _lib = None
 
@@ -49,6 +51,8 @@ def load(path: str | None = None):
     lib.fa2_fwd.restype = i
     lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa2_bwd.restype = i
+    lib.fa2_bwd_stages.argtypes = [ctypes.c_uint] + lib.fa2_bwd.argtypes
+    lib.fa2_bwd_stages.restype = i
     lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_bwd_workspace_bytes.restype = sz
     lib.fa2_validate_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
@@ -125,12 +129,15 @@ def workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, do: torch.Tensor, causal: bool = False,
-             scale: float | None = None, workspace: torch.Tensor | None = None):
+             scale: float | None = None, workspace: torch.Tensor | None = None,
+             grads=None, stages: int = BWD_ALL):
     """dQ, dK, dV of sum(do * o) for the forward above (P rebuilt from lse).
 
     Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) bf16.  A caller
     may pass a reusable uint8 ``workspace`` of at least
-    ``workspace_bytes(...)`` bytes (256-byte aligned).
+    ``workspace_bytes(...)`` bytes (256-byte aligned), preallocated output
+    tensors ``grads=(dq, dk, dv)``, and a subset of the launch ``stages``
+    (issued in order; the workspace must carry over between partial calls).
     """
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
@@ -144,11 +151,17 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    st = lib.fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                     _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d,
-                     int(bool(causal)), float(scale), _stream_handle(q))
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.dtype != torch.bfloat16 or t.shape != like.shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like its input")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    st = lib.fa2_bwd_stages(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv

@@ -109,6 +109,29 @@ fa2_status fa2_bwd(const void *Q, const void *K, const void *V, const void *O,
                    void *stream);
 
 /*
+ * The backward pass as its three launches, selected by a bit mask, with the
+ * same arguments and checks as fa2_bwd:
+ *   FA2_BWD_PREPROCESS  D = rowsum(dO o O) (section 4 symbol table of the
+ *                       FlashAttention-2 summary page) into the workspace,
+ *                       and the fp32 dQ accumulator set to zero;
+ *   FA2_BWD_MAIN        the K/V-tile loop: dK, dV written, dQ added into the
+ *                       accumulator with atomics (same page, sections 2 and 7);
+ *   FA2_BWD_FINALIZE    dQ = bf16(scale * accumulator).
+ * Running the stages in this order on one stream, with the same workspace
+ * untouched in between, is exactly fa2_bwd (mask FA2_BWD_ALL).  Stages may be
+ * issued by separate calls, e.g. to time or overlap them.  A mask with no
+ * known bit, or with bits outside FA2_BWD_ALL, is FA2_ERR_INVALID_ARGUMENT.
+ */
+#define FA2_BWD_PREPROCESS 1u
+#define FA2_BWD_MAIN 2u
+#define FA2_BWD_FINALIZE 4u
+#define FA2_BWD_ALL 7u
+fa2_status fa2_bwd_stages(unsigned stages, const void *Q, const void *K, const void *V,
+                          const void *O, const float *L, const void *dO, void *dQ, void *dK,
+                          void *dV, void *workspace, size_t workspace_bytes, int B, int Hq,
+                          int Hkv, int N, int d, int causal, float scale, void *stream);
+
+/*
  * The argument checks of fa2_fwd / fa2_bwd alone: no HIP call is made, so
  * they run without a GPU.  Same return codes as the full calls.
  */

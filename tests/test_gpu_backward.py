@@ -167,3 +167,19 @@ def test_bwd_geometric_rows():
     parity.check_bf16("geometric dQ", parity.bf16_to_f64(dq), rdq, working=wdq)
     parity.check_bf16("geometric dK", parity.bf16_to_f64(dk), rdk, working=wdk)
     parity.check_bf16("geometric dV", parity.bf16_to_f64(dv), rdv, working=wdv)
+
+
+def test_bwd_stages_in_separate_calls_equal_one_call():
+    from exact_io_aware_26_amd import fa2
+    qb, kb, vb, dob = inputs.attention_inputs(35, 1, 4, 2, 1100, 128, with_grad=True)
+    q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
+    o, L = fa2.forward(q, k, v, causal=True)
+    dq1, dk1, dv1 = fa2.backward(q, k, v, o, L, do, causal=True)
+    ws = torch.empty(fa2.workspace_bytes(1, 4, 2, 1100, 128), dtype=torch.uint8, device=q.device)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+    for st in (fa2.BWD_PREPROCESS, fa2.BWD_MAIN, fa2.BWD_FINALIZE):
+        fa2.backward(q, k, v, o, L, do, causal=True, workspace=ws, grads=grads, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(dk1.view(torch.int16), grads[1].view(torch.int16))
+    assert torch.equal(dv1.view(torch.int16), grads[2].view(torch.int16))
+    parity.check_bf16("dQ staged", parity.bf16_to_f64(grads[0]), parity.bf16_to_f64(dq1))
