@@ -239,8 +239,9 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
                           void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
                           int Hkv, int N, int d, int causal, float scale, void* stream) {
     g_last_error[0] = '\0';
-    if (stages == 0 || (stages & ~FA2_BWD_ALL) != 0)
-        return fail(FA2_ERR_INVALID_ARGUMENT, "stage mask must be a non-empty subset of FA2_BWD_ALL");
+    if ((stages & FA2_BWD_ALL) == 0 || (stages & ~(FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC)) != 0)
+        return fail(FA2_ERR_INVALID_ARGUMENT,
+                    "stage mask must hold at least one stage of FA2_BWD_ALL and no unknown bits");
     bool empty;
     Sizes sz;
     fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,

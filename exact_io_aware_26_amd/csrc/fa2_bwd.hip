@@ -89,9 +89,10 @@ template <> struct BwdCfg<128> { static constexpr int BC = 128, NW = 4, BR = 64;
 template <> struct BwdCfg<256> { static constexpr int BC = 64, NW = 2, BR = 32; static constexpr bool KV_REGS = false; };
 
 // ---------------------------------------------------------------------------------------------
-// bwd_pre: D_i = sum_d dO_id * O_id (fp32) and zero the dQ accumulator row.
+// bwd_pre: D_i = sum_d dO_id * O_id (fp32); zero the dQ accumulator row when dQ
+// is accumulated with atomics.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long rows, int zero_dq) {
     constexpr int LPR = D / 8;                 // lanes per row (8 bf16 each)
     constexpr int RPB = 256 / LPR;             // rows per block
     const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -107,9 +108,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
             acc = fmaf(u32_as_f32(x << 16), u32_as_f32(y << 16), acc);
             acc = fmaf(u32_as_f32(x & 0xffff0000u), u32_as_f32(y & 0xffff0000u), acc);
         }
-        float* z = p.dQacc + off;
-        *reinterpret_cast<u32x4*>(z) = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(z + 4) = u32x4{0, 0, 0, 0};
+        if (zero_dq) {
+            float* z = p.dQacc + off;
+            *reinterpret_cast<u32x4*>(z) = u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(z + 4) = u32x4{0, 0, 0, 0};
+        }
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * BwdCfg<D>::NW, 64 * BwdCfg<D>::NW),
                           amdgpu_waves_per_eu(1, 1)))
 void bwd_main_kernel(const BwdParams p) {
@@ -137,13 +140,13 @@ void bwd_main_kernel(const BwdParams p) {
     constexpr int kVBytes = KV_REGS ? 0 : BC * RB_D;
     constexpr int kQBytes = BR * RB_D;
     constexpr int kSBytes = BC * RB_Q;
-    __shared__ __attribute__((aligned(16))) char smem_raw[kKBytes + kVBytes + 2 * kQBytes + kSBytes + 2 * BR * 4];
+    __shared__ __attribute__((aligned(16))) char smem_raw[kKBytes + kVBytes + 2 * kQBytes + 2 * kSBytes + 2 * BR * 4];
     FA2_LDS char* Ks = (FA2_LDS char*)smem_raw;
     FA2_LDS char* Vs = Ks + kKBytes;
     FA2_LDS char* Qs = Vs + kVBytes;
     FA2_LDS char* dOs = Qs + kQBytes;
-    FA2_LDS char* dSt = dOs + kQBytes;
-    FA2_LDS float* Ls = (FA2_LDS float*)(dSt + kSBytes);
+    FA2_LDS char* dStBuf = dOs + kQBytes;      // two dS^T tiles: dQ runs one query tile behind
+    FA2_LDS float* Ls = (FA2_LDS float*)(dStBuf + 2 * kSBytes);
     FA2_LDS float* Dl = Ls + BR;
 
     const int tid = threadIdx.x;
@@ -245,17 +248,62 @@ void bwd_main_kernel(const BwdParams p) {
             }
         }
         if (tid < BR) {
-            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)N + qt0 + tid;
-            const bool in = qt0 + tid < N;
-            sl = in ? p.L[r] * kLog2e : kInf;   // rows past the end get P = 0
-            sd = in ? p.Dsum[r] : 0.f;
+            // Raw values from a clamped row; scaled and masked when written to LDS,
+            // so nothing here waits for these loads to land.
+            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)N + min(qt0 + tid, N - 1);
+            sl = p.L[r];
+            sd = p.Dsum[r];
+        }
+    };
+
+    // dQ of query tile `it` (BR x D): the waves split the 32x32 output blocks and
+    // reduce over all BC keys of the workgroup (dS^T and K by transposed LDS
+    // reads), then add into the fp32 accumulator with one atomic per element.
+    // Every wave issues the same fixed number of atomics: rows past the end
+    // carry exactly +0 (their P is 0) and go to the last valid row.
+    static_assert((NQB * NBD) % NW == 0, "dQ blocks must split evenly over the waves");
+    auto dq_tile = [&](int it) {
+        const int hq = hk * p.G + it / n_i;
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const FA2_LDS char* dSt = dStBuf + (it & 1) * kSBytes;
+        float* const dqh = p.dQacc + ((size_t)b * p.Hq + hq) * (size_t)N * D;   // uniform base
+        const bool full = qt0 + BR <= N;
+#pragma unroll
+        for (int tt = 0; tt < NQB * NBD / NW; ++tt) {
+            const int t = wave + tt * NW;
+            const int qb = t / NBD, db = t % NBD;
+            f32x16 acc = zero16();
+            int kk_end = KSKV;
+            if (CAUSAL) {
+                // keys beyond the block's last query contribute dS = 0
+                const int last_q = qt0 + 32 * qb + 31 - kv0;
+                kk_end = min(KSKV, last_q / 16 + 1);
+            }
+            for (int kk = 0; kk < kk_end; ++kk) {
+                const bf16x8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
+                const bf16x8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
+                acc = mfma32(a, bk, acc);
+            }
+            const int d = 32 * db + li;
+            const int row0 = qt0 + 32 * qb + 4 * g;
+            if (full) {
+                float* const base = dqh + (size_t)row0 * D + d;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    atomicAdd(base + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qg = min(row0 + 8 * (r >> 2) + (r & 3), N - 1);
+                    atomicAdd(dqh + (size_t)qg * D + d, acc[r]);
+                }
+            }
         }
     };
 
     if (PREFETCH && n_iter > 0) stage(0);
 
     for (int it = 0; it < n_iter; ++it) {
-        const int hq = hk * p.G + it / n_i;
         const int qt0 = (i_begin + it % n_i) * BR;
 
         // 1. query tile -> LDS (all waves are past barrier (B) of the previous
@@ -274,70 +322,75 @@ void bwd_main_kernel(const BwdParams p) {
             stage(it);
         }
         if (tid < BR) {
-            Ls[tid] = sl;
-            Dl[tid] = sd;
+            const bool in = qt0 + tid < N;
+            Ls[tid] = in ? sl * kLog2e : kInf;         // rows past the end get P = 0
+            Dl[tid] = in ? sd : 0.f;
         }
         __syncthreads();                               // (A) tile visible
-        if (PREFETCH && it + 1 < n_iter) stage(it + 1);  // next tile's loads in flight
 
-        // 2. S, P, dP, dS for this wave's keys; dV, dK updates; dS^T -> LDS
-        const bool wave_any = kw0 < N && !(CAUSAL && qt0 + BR - 1 < kw0);
-        if (wave_any) {
-            const bool need_mask = (CAUSAL && qt0 < kw0 + 32) || qt0 + BR > N || kw0 + 32 > N;
-            uint32_t pp[NQB][8], sp[NQB][8];
+        // 2. dQ of the previous tile (its dS^T is complete since barrier (B)); its
+        //    atomics, then the next tile's loads, get all of step 3 to land.
+        if (DQ_ATOMIC && it > 0) dq_tile(it - 1);
+        if (PREFETCH && it + 1 < n_iter) stage(it + 1);
+        FA2_LDS char* dSt = dStBuf + (it & 1) * kSBytes;
+
+        // 3. Per 32-row query block: S, dP (MFMA), P, dS (VALU), dS^T -> LDS, then
+        //    dV^T += dO^T P and dK^T += Q^T dS.  Every wave always runs (keys a
+        //    query tile cannot see get P = 0 from the mask), so the gradient
+        //    accumulators are updated unconditionally.
+        const bool need_mask = (CAUSAL && qt0 < kw0 + 32) || qt0 + BR > N || kw0 + 32 > N;
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                f32x16 s = zero16(), dp = zero16();
+        for (int qb = 0; qb < NQB; ++qb) {
+            f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const bf16x8 aq = row_operand<RB_D>(Qs, 32 * qb, 16 * ks, lane);
-                    const bf16x8 ao = row_operand<RB_D>(dOs, 32 * qb, 16 * ks, lane);
-                    bf16x8 bk, bv;
-                    if (KV_REGS) {
-                        bk = kf[KV_REGS ? ks : 0];
-                        bv = vf[KV_REGS ? ks : 0];
-                    } else {
-                        bk = row_operand<RB_D>(Ks, 32 * wave, 16 * ks, lane);
-                        bv = row_operand<RB_D>(Vs, 32 * wave, 16 * ks, lane);
-                    }
-                    s = mfma32(aq, bk, s);
-                    dp = mfma32(ao, bv, dp);
+            for (int ks = 0; ks < KSD; ++ks) {
+                const bf16x8 aq = row_operand<RB_D>(Qs, 32 * qb, 16 * ks, lane);
+                const bf16x8 ao = row_operand<RB_D>(dOs, 32 * qb, 16 * ks, lane);
+                bf16x8 bk, bv;
+                if (KV_REGS) {
+                    bk = kf[KV_REGS ? ks : 0];
+                    bv = vf[KV_REGS ? ks : 0];
+                } else {
+                    bk = row_operand<RB_D>(Ks, 32 * wave, 16 * ks, lane);
+                    bv = row_operand<RB_D>(Vs, 32 * wave, 16 * ks, lane);
                 }
+                s = mfma32(aq, bk, s);
+                dp = mfma32(ao, bv, dp);
+            }
+            if (need_mask) {
+                // keys above the diagonal or past the end: S = -inf, so P = 0
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int ql = 32 * qb + 8 * rq + 4 * g;      // local query of register 4*rq
-                    float lv[4], dv4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lv[e] = Ls[ql + e];
-                        dv4[e] = Dl[ql + e];
-                    }
-                    float pr[4], dsr[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * rq + e;
-                        float pv = exp2_fast(fmaf(s[r], p.c, -lv[e]));
-                        if (need_mask) {
-                            const int qg = qt0 + ql + e;
-                            if ((CAUSAL && kv > qg) || kv >= N) pv = 0.f;
-                        }
-                        pr[e] = pv;
-                        dsr[e] = pv * (dp[r] - dv4[e]);
-                    }
-                    pp[qb][2 * rq] = pack_bf16(pr[0], pr[1]);
-                    pp[qb][2 * rq + 1] = pack_bf16(pr[2], pr[3]);
-                    sp[qb][2 * rq] = pack_bf16(dsr[0], dsr[1]);
-                    sp[qb][2 * rq + 1] = pack_bf16(dsr[2], dsr[3]);
-                    // dS^T[key][query .. query+3]
-                    *reinterpret_cast<FA2_LDS u32x2*>(dSt + tile_off<RB_Q>(32 * wave + li, ql)) =
-                        u32x2{sp[qb][2 * rq], sp[qb][2 * rq + 1]};
+                for (int r = 0; r < 16; ++r) {
+                    const int qg = qt0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((CAUSAL && kv > qg) || kv >= N) s[r] = -kInf;
                 }
             }
+            uint32_t pp[8], sp[8];
 #pragma unroll
-            for (int kk = 0; kk < KSQ; ++kk) {
-                const int qb = kk >> 1, h = kk & 1;
-                const bf16x8 bp = as_bf16x8(u32x4{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2], pp[qb][4 * h + 3]});
-                const bf16x8 bs = as_bf16x8(u32x4{sp[qb][4 * h], sp[qb][4 * h + 1], sp[qb][4 * h + 2], sp[qb][4 * h + 3]});
+            for (int rq = 0; rq < 4; ++rq) {
+                const int ql = 32 * qb + 8 * rq + 4 * g;          // local query of register 4*rq
+                const f32x4 lv = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
+                const f32x4 dd = *reinterpret_cast<const FA2_LDS f32x4*>(Dl + ql);
+                float pr[4], dsr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rq + e;
+                    pr[e] = exp2_fast(fmaf(s[r], p.c, -lv[e]));
+                    dsr[e] = pr[e] * (dp[r] - dd[e]);
+                }
+                pp[2 * rq] = pack_bf16(pr[0], pr[1]);
+                pp[2 * rq + 1] = pack_bf16(pr[2], pr[3]);
+                sp[2 * rq] = pack_bf16(dsr[0], dsr[1]);
+                sp[2 * rq + 1] = pack_bf16(dsr[2], dsr[3]);
+                // dS^T[key][query .. query+3]
+                *reinterpret_cast<FA2_LDS u32x2*>(dSt + tile_off<RB_Q>(32 * wave + li, ql)) =
+                    u32x2{sp[2 * rq], sp[2 * rq + 1]};
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kk = 2 * qb + h;
+                const bf16x8 bp = as_bf16x8(u32x4{pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]});
+                const bf16x8 bs = as_bf16x8(u32x4{sp[4 * h], sp[4 * h + 1], sp[4 * h + 2], sp[4 * h + 3]});
 #pragma unroll
                 for (int db = 0; db < NBD; ++db) {
                     const bf16x8 ao = tr_operand<RB_D>(dOs, 16 * kk, 32 * db, lane);
@@ -346,39 +399,11 @@ void bwd_main_kernel(const BwdParams p) {
                     dk[db] = mfma32(aq, bs, dk[db]);
                 }
             }
-        } else {
-            // no key of this wave is visible from this query tile: its dS^T rows are zero
-#pragma unroll
-            for (int ch = 0; ch < RB_Q / 16; ++ch)
-                lds_store16(dSt + (32 * wave + li) * RB_Q + 16 * ch, u32x4{0, 0, 0, 0});
         }
-        __syncthreads();                               // (B) dS^T of all waves visible
+        __syncthreads();                               // (B) dS^T visible; Q/dO/L/D free
 
-        // 3. dQ tile (BR x D): waves split the 32x32 output blocks; reduce over all BC keys.
-        const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
-        for (int t = wave; t < NQB * NBD; t += NW) {
-            const int qb = t / NBD, db = t % NBD;
-            if (qt0 + 32 * qb >= N) continue;
-            f32x16 acc = zero16();
-            int kk_end = KSKV;
-            if (CAUSAL) {
-                // keys beyond the block's last query contribute dS = 0
-                const int last_q = qt0 + 32 * qb + 31 - kv0;
-                kk_end = min(KSKV, last_q / 16 + 1);
-            }
-            for (int kk = 0; kk < kk_end; ++kk) {
-                const bf16x8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
-                const bf16x8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
-                acc = mfma32(a, bk, acc);
-            }
-            const int d = 32 * db + li;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (qt0 + ql < N) atomicAdd(p.dQacc + (qrow0 + ql) * D + d, acc[r]);
-            }
-        }
     }
+    if (DQ_ATOMIC && n_iter > 0) dq_tile(n_iter - 1);
 
     // ---- epilogue: dV, dK (scaled) for this lane's key
     if (kv < N) {
@@ -395,6 +420,438 @@ void bwd_main_kernel(const BwdParams p) {
                 *reinterpret_cast<u32x2*>(dKr + d0) =
                     u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
                           pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bwd_pair: the K/V-tile loop for d = 64 and 128 with two waves per SIMD.
+//
+// Eight waves form four pairs; pair k owns keys 32k..32k+31 of the 128-key
+// tile.  For each 64-row query tile, wave h of a pair (h = 0, 1) computes S,
+// dP, P and dS for query block h (32 rows, full head dim) and publishes P and
+// dS to LDS; then each wave accumulates dV and dK for ITS HALF of the head
+// dim from both query blocks.  So no MFMA is duplicated, the gradient
+// accumulators take half the registers, and two waves fit on every SIMD
+// (one MFMA stream can run while the other wave does softmax or LDS work).
+//
+// P^T and dS^T tiles are stored [key][query] with the query columns of every
+// 16-group in bit-swapped order (bits 2 and 3 exchanged): then a plain
+// 16-byte row read returns exactly the 8 queries a lane must hold as the
+// MFMA B operand, in the order of the transposed-read A operands
+// (4g + 0..3, 8 + 4g + 0..3 within a 16-query step).  dQ reads dS^T with
+// transposed reads, so its output rows come out in that swapped order and
+// the atomics map them back.
+//
+// Two barriers per query tile: Q/dO/L/D are double-buffered, dS^T is
+// double-buffered (dQ runs one tile behind), P^T is single-buffered (it is
+// consumed before the next tile's first barrier).
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+template <int D, bool CAUSAL, bool DQ_ATOMIC>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void bwd_pair_kernel(const BwdParams p) {
+    constexpr int BC = 128, NW = 8, NT = 512, BR = 64;
+    constexpr int RB_D = 2 * D;        // bytes per row of K / Q / dO tiles
+    constexpr int RB_Q = 2 * BR;       // bytes per row of the P^T / dS^T tiles
+    constexpr int KSD = D / 16;        // reduction steps over the head dim (S, dP)
+    constexpr int NBH = D / 64;        // 32-wide head-dim blocks per half
+    constexpr int KSKV = BC / 16;      // reduction steps over the keys (dQ)
+    constexpr int NBD = D / 32;        // 32-wide head-dim blocks (dQ)
+    constexpr int kKBytes = BC * RB_D;
+    constexpr int kQBytes = BR * RB_D;
+    constexpr int kSBytes = BC * RB_Q;
+    __shared__ __attribute__((aligned(16))) char smem_raw[kKBytes + 4 * kQBytes + 3 * kSBytes + 4 * BR * 4];
+    FA2_LDS char* Ks = (FA2_LDS char*)smem_raw;
+    FA2_LDS char* QObuf = Ks + kKBytes;             // [2][Q tile, dO tile]
+    FA2_LDS char* dStBuf = QObuf + 4 * kQBytes;     // [2] dS^T
+    FA2_LDS char* Pt = dStBuf + 2 * kSBytes;        // P^T
+    FA2_LDS float* LDbuf = (FA2_LDS float*)(Pt + kSBytes);  // [2][L row, D row]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+    const int kvb = wave & 3;          // key block of the pair
+    const int h = wave >> 2;           // query block (phase A) and head-dim half (phase B)
+
+    const int BHk = p.B * p.Hkv;
+    const int kvtile = blockIdx.x / BHk;
+    const int bh = blockIdx.x - kvtile * BHk;
+    const int b = bh / p.Hkv;
+    const int hk = bh - b * p.Hkv;
+    const int N = p.N;
+    const int kv0 = kvtile * BC;
+    const int kw0 = kv0 + 32 * kvb;
+    const int kv = kw0 + li;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+
+    // K tile -> LDS (dQ operand); this pair's K/V rows -> VGPRs (S, dP operands)
+    {
+        constexpr int CPR = D / 8;
+        for (int c = tid; c < BC * CPR; c += NT) {
+            const int row = c / CPR, col = (c % CPR) * 8;
+            u32x4 kx = {0, 0, 0, 0};
+            if (kv0 + row < N) kx = global_load16(p.K + khead + (size_t)(kv0 + row) * D + col);
+            lds_store16(Ks + tile_off<RB_D>(row, col), kx);
+        }
+    }
+    bf16x8 kf[KSD], vf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+        if (kv < N) {
+            kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
+            vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
+        }
+        kf[ks] = as_bf16x8(kx);
+        vf[ks] = as_bf16x8(vx);
+    }
+    f32x16 dv[NBH], dk[NBH];
+#pragma unroll
+    for (int i = 0; i < NBH; ++i) {
+        dv[i] = zero16();
+        dk[i] = zero16();
+    }
+
+    const int n_qt = (N + BR - 1) / BR;
+    const int i_begin = CAUSAL ? kv0 / BR : 0;
+    const int n_i = n_qt - i_begin;
+    const int n_iter = n_i * p.G;
+
+    // Next query tile staged in VGPRs while the current one is computed.
+    constexpr int QCH = BR * D / 8;
+    constexpr int QPT = QCH / NT;
+    static_assert(QPT >= 1 && QCH % NT == 0, "query tile / threads mismatch");
+    u32x4 sq[QPT], so[QPT];
+    float sl = 0.f, sd = 0.f;
+    auto stage = [&](int it) {
+        const int hq = hk * p.G + it / n_i;
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+            const int c = tid + k * NT;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            sq[k] = u32x4{0, 0, 0, 0};
+            so[k] = u32x4{0, 0, 0, 0};
+            if (qt0 + row < N) {
+                sq[k] = global_load16(p.Q + qhead + (size_t)(qt0 + row) * D + col);
+                so[k] = global_load16(p.dO + qhead + (size_t)(qt0 + row) * D + col);
+            }
+        }
+        if (tid < BR) {   // raw values from a clamped row; scaled and masked when stored
+            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)N + min(qt0 + tid, N - 1);
+            sl = p.L[r];
+            sd = p.Dsum[r];
+        }
+    };
+
+    // dQ of query tile `it`: one 32x32 output block per wave (d = 128; waves 0-3
+    // for d = 64), reduced over the 128 keys; one atomic per element.
+    constexpr int NDQ = 2 * NBD;       // output blocks per query tile
+    auto dq_tile = [&](int it) {
+        if (wave >= NDQ) return;
+        const int hq = hk * p.G + it / n_i;
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const FA2_LDS char* dSt = dStBuf + (it & 1) * kSBytes;
+        const int qb = wave & 1, db = wave >> 1;
+        f32x16 acc = zero16();
+        int kk_end = KSKV;
+        if (CAUSAL) kk_end = min(KSKV, (qt0 + 32 * qb + 31 - kv0) / 16 + 1);
+        for (int kk = 0; kk < kk_end; ++kk) {
+            const bf16x8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
+            const bf16x8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
+            acc = mfma32(a, bk, acc);
+        }
+        // Output row i = 8*(r/4) + 4g + r%4 holds dS^T column i, i.e. query swap23(i).
+        float* const dqh = p.dQacc + ((size_t)b * p.Hq + hq) * (size_t)N * D;
+        const int d = 32 * db + li;
+        const int row0 = qt0 + 32 * qb + 8 * g;
+        if (qt0 + BR <= N) {
+            float* const base = dqh + (size_t)row0 * D + d;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                atomicAdd(base + (16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3)) * D, acc[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qg = min(row0 + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3), N - 1);
+                atomicAdd(dqh + (size_t)qg * D + d, acc[r]);   // rows past the end add +0
+            }
+        }
+    };
+
+    if (n_iter > 0) stage(0);
+    for (int it = 0; it < n_iter; ++it) {
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const int buf = it & 1;
+        FA2_LDS char* Qs = QObuf + buf * 2 * kQBytes;
+        FA2_LDS char* dOs = Qs + kQBytes;
+        FA2_LDS float* Ls = LDbuf + buf * 2 * BR;
+        FA2_LDS float* Dl = Ls + BR;
+        FA2_LDS char* dSt = dStBuf + buf * kSBytes;
+
+        // 1. staged tile -> LDS buffer `buf` (last read two tiles ago)
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+            const int c = tid + k * NT;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            lds_store16(Qs + tile_off<RB_D>(row, col), sq[k]);
+            lds_store16(dOs + tile_off<RB_D>(row, col), so[k]);
+        }
+        if (tid < BR) {
+            const bool in = qt0 + tid < N;
+            Ls[tid] = in ? sl * kLog2e : kInf;   // rows past the end get P = 0
+            Dl[tid] = in ? sd : 0.f;
+        }
+        __syncthreads();                         // (A)
+
+        // 2. dQ of the previous tile, then the next tile's loads; both land during 3-4.
+        if (DQ_ATOMIC && it > 0) dq_tile(it - 1);
+        if (it + 1 < n_iter) stage(it + 1);
+
+        // 3. query block h: S, dP, P, dS for this pair's keys; publish P^T, dS^T.
+        {
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const bf16x8 aq = row_operand<RB_D>(Qs, 32 * h, 16 * ks, lane);
+                const bf16x8 ao = row_operand<RB_D>(dOs, 32 * h, 16 * ks, lane);
+                s = mfma32(aq, kf[ks], s);
+                dp = mfma32(ao, vf[ks], dp);
+            }
+            const bool need_mask = (CAUSAL && qt0 + 32 * h < kw0 + 32) || qt0 + 32 * h + 32 > N || kw0 + 32 > N;
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qg = qt0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((CAUSAL && kv > qg) || kv >= N) s[r] = -kInf;
+                }
+            }
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int ql = 32 * h + 8 * rq + 4 * g;          // local query of register 4*rq
+                const f32x4 lv = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
+                const f32x4 dd = *reinterpret_cast<const FA2_LDS f32x4*>(Dl + ql);
+                float pr[4], dsr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rq + e;
+                    pr[e] = exp2_fast(fmaf(s[r], p.c, -lv[e]));
+                    dsr[e] = pr[e] * (dp[r] - dd[e]);
+                }
+                const int pos = 32 * h + swap23(8 * rq + 4 * g);   // 4 queries stay contiguous
+                const int off = tile_off<RB_Q>(32 * kvb + li, pos);
+                *reinterpret_cast<FA2_LDS u32x2*>(Pt + off) = u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
+                *reinterpret_cast<FA2_LDS u32x2*>(dSt + off) = u32x2{pack_bf16(dsr[0], dsr[1]), pack_bf16(dsr[2], dsr[3])};
+            }
+        }
+        __syncthreads();                         // (X) P^T, dS^T of both query blocks visible
+
+        // 4. dV^T += dO^T P and dK^T += Q^T dS over both query blocks, this wave's half of d.
+#pragma unroll
+        for (int kk = 0; kk < BR / 16; ++kk) {
+            const int row = 32 * kvb + li;
+            const int col = 16 * kk + 8 * g;
+            const bf16x8 bp = as_bf16x8(lds_load16(Pt + tile_off<RB_Q>(row, col)));
+            const bf16x8 bs = as_bf16x8(lds_load16(dSt + tile_off<RB_Q>(row, col)));
+#pragma unroll
+            for (int j = 0; j < NBH; ++j) {
+                const int dcol = (D / 2) * h + 32 * j;
+                const bf16x8 ao = tr_operand<RB_D>(dOs, 16 * kk, dcol, lane);
+                dv[j] = mfma32(ao, bp, dv[j]);
+                const bf16x8 aq = tr_operand<RB_D>(Qs, 16 * kk, dcol, lane);
+                dk[j] = mfma32(aq, bs, dk[j]);
+            }
+        }
+    }
+    if (DQ_ATOMIC && n_iter > 0) {
+        __syncthreads();                         // dS^T of the last tile complete
+        dq_tile(n_iter - 1);
+    }
+
+    // epilogue: this lane's key, this wave's half of the head dim
+    if (kv < N) {
+        uint16_t* dVr = p.dV + khead + (size_t)kv * D;
+        uint16_t* dKr = p.dK + khead + (size_t)kv * D;
+#pragma unroll
+        for (int j = 0; j < NBH; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d0 = (D / 2) * h + 32 * j + 8 * rq + 4 * g;
+                *reinterpret_cast<u32x2*>(dVr + d0) =
+                    u32x2{pack_bf16(dv[j][4 * rq], dv[j][4 * rq + 1]),
+                          pack_bf16(dv[j][4 * rq + 2], dv[j][4 * rq + 3])};
+                *reinterpret_cast<u32x2*>(dKr + d0) =
+                    u32x2{pack_bf16(dk[j][4 * rq] * p.scale, dk[j][4 * rq + 1] * p.scale),
+                          pack_bf16(dk[j][4 * rq + 2] * p.scale, dk[j][4 * rq + 3] * p.scale)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bwd_dq: dQ without atomics, one workgroup per 128 query rows (4 waves x 32).
+//
+// The dQ contribution of every K/V tile is summed in registers instead of
+// through global atomics: each wave keeps its query rows (Q and dO as MFMA
+// operands, L and D as one value per lane) and streams K/V tiles through
+// double-buffered LDS, recomputing what it needs, all transposed so that
+// each lane owns one query row:
+//     S^T  = K Q^T,   P^T = exp2(c S^T - L log2 e)          (masked on the diagonal)
+//     dP^T = V dO^T,  dS^T = P^T o (dP^T - D)
+//     dQ^T += K^T dS^T          (K^T by transposed LDS reads, dS^T from registers)
+// and finally writes dQ = bf16(scale * dQ) once.  This costs the S and dP
+// products a second time, and in exchange the result is deterministic.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+void bwd_dq_kernel(const BwdParams p) {
+    constexpr int BC = D == 256 ? 32 : 64, BRQ = 128, NT = 256;
+    constexpr int RB_D = 2 * D;
+    constexpr int NBS = BC / 32;       // 32-key blocks per tile
+    constexpr int KSD = D / 16;
+    constexpr int NBD = D / 32;
+    constexpr int kTileBytes = BC * RB_D;
+    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kTileBytes];
+    FA2_LDS char* smem = (FA2_LDS char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    // Heaviest causal query tiles first; heads of one level on consecutive ids.
+    const int n_qtiles = (p.N + BRQ - 1) / BRQ;
+    const int BH = p.B * p.Hq;
+    const int level = blockIdx.x / BH;
+    const int bh = blockIdx.x - level * BH;
+    const int qtile = n_qtiles - 1 - level;
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hk = hq / p.G;
+    const int N = p.N;
+    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+    const uint16_t* Kh = p.K + khead;
+    const uint16_t* Vh = p.V + khead;
+    const int q0 = qtile * BRQ;
+    const int wq0 = q0 + 32 * wave;
+    const int q = wq0 + li;
+    const bool wave_live = wq0 < N;
+
+    bf16x8 qf[KSD], of[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+        if (q < N) {
+            a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
+            c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
+        }
+        qf[ks] = as_bf16x8(a);
+        of[ks] = as_bf16x8(c);
+    }
+    const size_t row = ((size_t)b * p.Hq + hq) * (size_t)N + min(q, N - 1);
+    const float l2 = q < N ? p.L[row] * kLog2e : kInf;   // rows past the end: P = 0
+    const float dq_d = q < N ? p.Dsum[row] : 0.f;
+
+    int n_kv = (N + BC - 1) / BC;
+    if (CAUSAL) n_kv = (min(q0 + BRQ, N) - 1) / BC + 1;
+
+    constexpr int CPR = D / 8;
+    constexpr int PER = BC * CPR / NT;
+    static_assert(PER >= 1 && BC * CPR % NT == 0, "tile / threads mismatch");
+    u32x4 sk[PER], sv[PER];
+    auto load = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CPR, col = (c % CPR) * 8;
+            sk[i] = u32x4{0, 0, 0, 0};
+            sv[i] = u32x4{0, 0, 0, 0};
+            if (kv0 + r < N) {
+                sk[i] = global_load16(Kh + (size_t)(kv0 + r) * D + col);
+                sv[i] = global_load16(Vh + (size_t)(kv0 + r) * D + col);
+            }
+        }
+    };
+    auto store = [&](FA2_LDS char* Ks, FA2_LDS char* Vs) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CPR, col = (c % CPR) * 8;
+            lds_store16(Ks + tile_off<RB_D>(r, col), sk[i]);
+            lds_store16(Vs + tile_off<RB_D>(r, col), sv[i]);
+        }
+    };
+
+    f32x16 acc[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) acc[i] = zero16();
+
+    load(0);
+    store(smem, smem + kTileBytes);
+    __syncthreads();
+    for (int j = 0; j < n_kv; ++j) {
+        const int kv0 = j * BC;
+        FA2_LDS char* Ks = smem + (j & 1) * (2 * kTileBytes);
+        FA2_LDS char* Vs = Ks + kTileBytes;
+        const bool has_next = j + 1 < n_kv;
+        if (has_next) load(kv0 + BC);
+
+        if (wave_live && !(CAUSAL && kv0 > wq0 + 31)) {
+            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs) {          // one 32-key block at a time
+                f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    s = mfma32(row_operand<RB_D>(Ks, 32 * bs, 16 * ks, lane), qf[ks], s);
+                    dp = mfma32(row_operand<RB_D>(Vs, 32 * bs, 16 * ks, lane), of[ks], dp);
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if ((CAUSAL && kv > q) || kv >= N) s[r] = -kInf;
+                    }
+                }
+                uint32_t dsp[8];
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = exp2_fast(fmaf(s[r], p.c, -l2));
+                    const float p1 = exp2_fast(fmaf(s[r + 1], p.c, -l2));
+                    dsp[r >> 1] = pack_bf16(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kk = 2 * bs + hh;
+                    const bf16x8 bds = as_bf16x8(u32x4{dsp[4 * hh], dsp[4 * hh + 1], dsp[4 * hh + 2], dsp[4 * hh + 3]});
+#pragma unroll
+                    for (int db = 0; db < NBD; ++db)
+                        acc[db] = mfma32(tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane), bds, acc[db]);
+                }
+            }
+        }
+        if (has_next) {
+            FA2_LDS char* Kn = smem + ((j + 1) & 1) * (2 * kTileBytes);
+            store(Kn, Kn + kTileBytes);
+        }
+        __syncthreads();
+    }
+
+    if (wave_live && q < N) {
+        uint16_t* dQr = p.dQ + qhead + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NBD; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d0 = 32 * db + 8 * rq + 4 * g;
+                *reinterpret_cast<u32x2*>(dQr + d0) =
+                    u32x2{pack_bf16(acc[db][4 * rq] * p.scale, acc[db][4 * rq + 1] * p.scale),
+                          pack_bf16(acc[db][4 * rq + 2] * p.scale, acc[db][4 * rq + 3] * p.scale)};
             }
     }
 }
@@ -419,27 +876,47 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream) {
     BwdParams arg = p;
     const long rows = (long)p.B * p.Hq * p.N;
+    const bool atomic_dq = (stages & 8u) != 0;
     if (stages & 1u) {
         constexpr int RPB = 256 / (D / 8);
         long rows_arg = rows;
-        void* args[] = {&arg, &rows_arg};
+        int zero = atomic_dq ? 1 : 0;
+        void* args[] = {&arg, &rows_arg, &zero};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_pre_kernel<D>),
                                        dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
     if (stages & 2u) {
-        constexpr int BC = BwdCfg<D>::BC;
-        const long grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
         void* args[] = {&arg};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL>),
-                                       dim3((unsigned)grid), dim3(64 * BwdCfg<D>::NW), args, 0, stream);
+        const void* fn;
+        long grid;
+        unsigned threads;
+        if constexpr (D <= 128) {
+            fn = atomic_dq ? reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>)
+                           : reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, false>);
+            grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
+            threads = 512;
+        } else {
+            fn = atomic_dq ? reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>)
+                           : reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, false>);
+            constexpr int BC = BwdCfg<D>::BC;
+            grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
+            threads = 64 * BwdCfg<D>::NW;
+        }
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
         if (e != hipSuccess) return e;
     }
     if (stages & 4u) {
-        long n8 = rows * D / 8;
-        void* args[] = {&arg, &n8};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_convert_kernel),
-                               dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
+        if (atomic_dq) {
+            long n8 = rows * D / 8;
+            void* args[] = {&arg, &n8};
+            return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_convert_kernel),
+                                   dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
+        }
+        void* args[] = {&arg};
+        const long grid = (long)p.B * p.Hq * ((p.N + 127) / 128);
+        return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>),
+                               dim3((unsigned)grid), dim3(256), args, 0, stream);
     }
     return hipSuccess;
 }

@@ -37,7 +37,9 @@ struct BwdParams {
 constexpr int kFwdRows = 128;
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
-// stages: bit 0 preprocess (D, zero the dQ accumulator), bit 1 main loop, bit 2 dQ convert.
+// stages: bit 0 preprocess (D; zeroes the dQ accumulator in atomic mode), bit 1 the K/V-tile
+// loop (dK, dV; plus dQ atomics in atomic mode), bit 2 dQ (its own pass, or the
+// accumulator's conversion in atomic mode); bit 3 selects atomic mode.
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream);
 
 }  // namespace fa2

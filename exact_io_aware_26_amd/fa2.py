@@ -25,7 +25,7 @@ FA2_ERR_HIP = 3
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_bwd_workspace_bytes",
            "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string", "fa2_last_error")
 
-BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL = 1, 2, 4, 7
+BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
 
 _lib = None
 

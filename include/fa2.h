@@ -5,8 +5,9 @@
  * pass tiles the query rows across workgroups, streams K/V tiles through LDS
  * and keeps an online softmax with a deferred rescale of an unnormalized fp32
  * accumulator, emitting the per-row logsumexp L = m + log(l); the backward
- * pass rebuilds P = exp(S - L) from L and produces dQ, dK, dV, looping over
- * K/V tiles on the outside and accumulating dQ in fp32 with atomics.
+ * pass rebuilds P = exp(S - L) from L and produces dK, dV looping over K/V
+ * tiles on the outside, and dQ either in a separate pass over query tiles
+ * (default) or with fp32 atomics inside the K/V loop.
  * (FlashAttention-2 summary page, zhaifeiyue.github.io: section 2 "Q2
  * method" -- deferred rescaling, logsumexp, sequence parallelism, split-Q;
  * section 3 "Target operation" -- O = softmax(QK^T)V, optional causal mask,
@@ -46,9 +47,9 @@
  * synchronization with the stream, not as a return value.  The library is
  * thread-safe (no mutable global state beyond a per-thread error message).
  *
- * Determinism: the forward pass is bitwise reproducible.  The backward
- * pass's dQ is summed with fp32 atomics and is reproducible only up to the
- * order of those additions; dK and dV are reproducible.
+ * Determinism: the forward pass and fa2_bwd are bitwise reproducible.  The
+ * optional atomic-dQ mode of fa2_bwd_stages sums dQ with fp32 atomics and is
+ * reproducible only up to the order of those additions.
  */
 #ifndef FA2_H
 #define FA2_H
@@ -98,6 +99,8 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *   summed over the Hq/Hkv query heads sharing each key/value head).
  *   workspace: caller-allocated device memory, 256-byte aligned, of at least
  *   fa2_bwd_workspace_bytes(...) bytes; contents undefined on entry and exit.
+ *   (The default path uses only its D part; the atomic mode of
+ *   fa2_bwd_stages also uses the dQ accumulator.)
  * Errors: as fa2_fwd, plus FA2_ERR_INVALID_ARGUMENT when the workspace is
  * NULL, misaligned or too small, or when an output aliases an input or
  * another output.
@@ -112,20 +115,31 @@ fa2_status fa2_bwd(const void *Q, const void *K, const void *V, const void *O,
  * The backward pass as its three launches, selected by a bit mask, with the
  * same arguments and checks as fa2_bwd:
  *   FA2_BWD_PREPROCESS  D = rowsum(dO o O) (section 4 symbol table of the
- *                       FlashAttention-2 summary page) into the workspace,
- *                       and the fp32 dQ accumulator set to zero;
- *   FA2_BWD_MAIN        the K/V-tile loop: dK, dV written, dQ added into the
- *                       accumulator with atomics (same page, sections 2 and 7);
- *   FA2_BWD_FINALIZE    dQ = bf16(scale * accumulator).
- * Running the stages in this order on one stream, with the same workspace
- * untouched in between, is exactly fa2_bwd (mask FA2_BWD_ALL).  Stages may be
- * issued by separate calls, e.g. to time or overlap them.  A mask with no
- * known bit, or with bits outside FA2_BWD_ALL, is FA2_ERR_INVALID_ARGUMENT.
+ *                       FlashAttention-2 summary page) into the workspace;
+ *   FA2_BWD_MAIN        the loop over K/V tiles that writes dK and dV
+ *                       (same page, section 2: the backward's outer loop runs
+ *                       over K/V column blocks);
+ *   FA2_BWD_FINALIZE    dQ.
+ * By default dQ has its own pass (one workgroup per query tile summing the
+ * contributions of all K/V tiles in registers; S and dP are recomputed),
+ * which is deterministic and, on this GPU, faster than the alternative.
+ * With FA2_BWD_DQ_ATOMIC also set -- the pages' design (same page, section
+ * 7) -- the K/V loop adds every tile's dQ contribution into an fp32
+ * accumulator in the workspace with atomic adds (PREPROCESS zeroes it,
+ * FINALIZE converts it to bf16); dQ is then reproducible only up to the
+ * order of those additions.  The mode bit must be the same in every call
+ * of one backward pass.
+ * Running the three stages in order on one stream, with the same workspace
+ * untouched in between, is exactly fa2_bwd (mask FA2_BWD_ALL) or its atomic
+ * variant (FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC).  Stages may be issued by
+ * separate calls, e.g. to time or overlap them.  A mask without any stage
+ * bit, or with bits other than these four, is FA2_ERR_INVALID_ARGUMENT.
  */
 #define FA2_BWD_PREPROCESS 1u
 #define FA2_BWD_MAIN 2u
 #define FA2_BWD_FINALIZE 4u
 #define FA2_BWD_ALL 7u
+#define FA2_BWD_DQ_ATOMIC 8u
 fa2_status fa2_bwd_stages(unsigned stages, const void *Q, const void *K, const void *V,
                           const void *O, const float *L, const void *dO, void *dQ, void *dK,
                           void *dV, void *workspace, size_t workspace_bytes, int B, int Hq,

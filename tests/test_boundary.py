@@ -191,10 +191,10 @@ def test_full_entry_points_reject_before_any_hip_call(lib):
 def test_bwd_stage_mask(lib):
     p = [addr(i) for i in range(10)]
     ws = ws_bytes(lib)
-    for bad in (0, 8, 9, 15, 0xFFFFFFFF):
+    for bad in (0, 8, 16, 17, 0xFFFFFFFF):
         assert lib.fa2_bwd_stages(bad, *p, ws, 2, 4, 2, 100, 128, 1, 0.125, None) == INVALID
     # valid masks go on to the argument checks (here: an unsupported head dim)
-    for good in (1, 2, 3, 4, 5, 6, 7):
+    for good in (1, 2, 3, 4, 5, 6, 7, 9, 10, 15):
         assert lib.fa2_bwd_stages(good, *p, ws, 2, 4, 2, 100, 96, 1, 0.125, None) == UNSUPPORTED
 
 

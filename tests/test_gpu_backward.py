@@ -28,22 +28,25 @@ def _gpu():
     fa2.load()
 
 
-def run_fwd_bwd(qb, kb, vb, dob, causal, scale=None):
+def run_fwd_bwd(qb, kb, vb, dob, causal, scale=None, atomic=False):
     from exact_io_aware_26_amd import fa2
     q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
     o, L = fa2.forward(q, k, v, causal=causal, scale=scale)
     nbytes = fa2.workspace_bytes(*q.shape[:2], k.shape[1], *q.shape[2:])
-    # Workspace deliberately full of garbage: its contents are undefined on entry.
+    # Workspace and outputs deliberately full of garbage: the kernels must overwrite them.
     ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=q.device)
-    dq, dk, dv = fa2.backward(q, k, v, o, L, do, causal=causal, scale=scale, workspace=ws)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
+    dq, dk, dv = fa2.backward(q, k, v, o, L, do, causal=causal, scale=scale, workspace=ws,
+                              grads=grads, stages=stages)
     torch.cuda.synchronize()
     return o, L, dq, dk, dv
 
 
-def full_case(seed, B, Hq, Hkv, N, d, causal, scale=None):
-    log(f"[bwd] seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+def full_case(seed, B, Hq, Hkv, N, d, causal, scale=None, atomic=False):
+    log(f"[bwd] seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} atomic_dq={atomic}")
     qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True)
-    _, _, dq, dk, dv = run_fwd_bwd(qb, kb, vb, dob, causal, scale)
+    _, _, dq, dk, dv = run_fwd_bwd(qb, kb, vb, dob, causal, scale, atomic)
     q64, k64, v64, do64 = (inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb, dob))
     sc = scale or 1.0 / math.sqrt(d)
     rdq, rdk, rdv, _ = orc.backward(q64, k64, v64, do64, causal, sc)
@@ -72,6 +75,17 @@ def test_bwd_small_sweep(B, Hq, Hkv, N, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_multi_tile(N, d, causal):
     full_case(8, 1, 2, 1, N, d, causal)
+
+
+# The atomic-dQ mode (dQ summed with fp32 atomics inside the K/V loop).
+ATOMIC_CASES = [(1, 1, 1, 2, 64, True), (2, 4, 2, 65, 128, True), (1, 4, 1, 130, 256, True),
+                (2, 8, 8, 127, 64, False), (1, 2, 1, 1000, 128, True), (1, 2, 1, 2048, 128, False),
+                (1, 2, 2, 1000, 256, False), (1, 4, 2, 2048, 64, True)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", ATOMIC_CASES)
+def test_bwd_atomic_dq_mode(B, Hq, Hkv, N, d, causal):
+    full_case(300 + N + d, B, Hq, Hkv, N, d, causal, atomic=True)
 
 
 def head_case(w, heads):
@@ -127,10 +141,14 @@ def test_bwd_causal_first_row_and_determinism():
     _, _, dq2, dk2, dv2 = run_fwd_bwd(qb, kb, vb, dob, True)
     # Query 0 sees only key 0 with P = 1, so dS_00 = dP_00 - D_0 = 0 up to fp32 rounding.
     assert float(dq1[:, :, 0].float().abs().max()) <= 1e-3
-    # dK, dV are summed in a fixed order: bitwise reproducible.  dQ uses atomics.
-    assert torch.equal(dk1.view(torch.int16), dk2.view(torch.int16))
-    assert torch.equal(dv1.view(torch.int16), dv2.view(torch.int16))
-    parity.check_bf16("dQ repeat", parity.bf16_to_f64(dq1), parity.bf16_to_f64(dq2))
+    # The default backward sums everything in a fixed order: bitwise reproducible.
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # The atomic mode agrees with it (dQ up to the order of its fp32 additions).
+    _, _, dq3, dk3, dv3 = run_fwd_bwd(qb, kb, vb, dob, True, atomic=True)
+    assert torch.equal(dk1.view(torch.int16), dk3.view(torch.int16))
+    assert torch.equal(dv1.view(torch.int16), dv3.view(torch.int16))
+    parity.check_bf16("dQ atomic vs separate pass", parity.bf16_to_f64(dq3), parity.bf16_to_f64(dq1))
 
 
 def test_bwd_gqa_equals_summed_repeated_heads():
@@ -169,17 +187,20 @@ def test_bwd_geometric_rows():
     parity.check_bf16("geometric dV", parity.bf16_to_f64(dv), rdv, working=wdv)
 
 
-def test_bwd_stages_in_separate_calls_equal_one_call():
+@pytest.mark.parametrize("mode", [0, 8], ids=["separate_dq", "atomic_dq"])
+def test_bwd_stages_in_separate_calls_equal_one_call(mode):
     from exact_io_aware_26_amd import fa2
     qb, kb, vb, dob = inputs.attention_inputs(35, 1, 4, 2, 1100, 128, with_grad=True)
     q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
     o, L = fa2.forward(q, k, v, causal=True)
-    dq1, dk1, dv1 = fa2.backward(q, k, v, o, L, do, causal=True)
+    dq1, dk1, dv1 = fa2.backward(q, k, v, o, L, do, causal=True, stages=fa2.BWD_ALL | mode)
     ws = torch.empty(fa2.workspace_bytes(1, 4, 2, 1100, 128), dtype=torch.uint8, device=q.device)
     grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
     for st in (fa2.BWD_PREPROCESS, fa2.BWD_MAIN, fa2.BWD_FINALIZE):
-        fa2.backward(q, k, v, o, L, do, causal=True, workspace=ws, grads=grads, stages=st)
+        fa2.backward(q, k, v, o, L, do, causal=True, workspace=ws, grads=grads, stages=st | mode)
     torch.cuda.synchronize()
     assert torch.equal(dk1.view(torch.int16), grads[1].view(torch.int16))
     assert torch.equal(dv1.view(torch.int16), grads[2].view(torch.int16))
+    if mode == 0:
+        assert torch.equal(dq1.view(torch.int16), grads[0].view(torch.int16))
     parity.check_bf16("dQ staged", parity.bf16_to_f64(grads[0]), parity.bf16_to_f64(dq1))
