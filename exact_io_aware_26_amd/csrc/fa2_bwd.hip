@@ -45,14 +45,16 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kInf = __builtin_huge_valf();
 
-// Swizzle of the 16-byte chunk index of an LDS row holding RB bytes.  Rows
-// are read either as 8 consecutive rows x 32 bytes (MFMA row operands) or as
-// 8 consecutive rows x 64 bytes (transposed reads); both hit distinct banks.
-// (Rows of 64 bytes need none: four consecutive rows already span all banks.)
+// Swizzle of the 16-byte chunk index of an LDS row holding RB bytes.  The
+// LDS serves a 16-byte-per-lane read 16 lanes per clock and an 8-byte read
+// 32 lanes per clock (64 banks x 4 bytes).  Rows are read either as 16
+// consecutive rows x one chunk (MFMA row operands) or as 4 consecutive rows
+// x 4 chunks (transposed reads); this XOR pattern puts both on 64 distinct
+// banks for 64-, 128-, 256- and 512-byte rows.
 template <int RB> __device__ __forceinline__ int swz(int row) {
-    return RB == 64 ? 0
-         : RB == 128 ? 4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)
-                     : 4 * (row & 3) + 2 * ((row >> 2) & 1);
+    return RB == 64 ? ((row >> 2) & 3)
+         : RB == 128 ? 4 * ((row >> 1) & 1) + ((row >> 2) & 3)
+                     : 4 * (row & 3) + ((row >> 2) & 3);
 }
 
 // Byte offset of element `col` (bf16) in row `row` of a swizzled tile with RB bytes per row.
@@ -714,8 +716,11 @@ void bwd_dq_kernel(const BwdParams p) {
     constexpr int KSD = D / 16;
     constexpr int NBD = D / 32;
     constexpr int kTileBytes = BC * RB_D;
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kTileBytes];
-    FA2_LDS char* smem = (FA2_LDS char*)smem_raw;
+    // Two K/V buffers as four distinct LDS objects: with the loop unrolled by
+    // two, every read names a buffer that differs from the one the in-flight
+    // tile is written to, so the compiler adds no wait on that tile before the
+    // transposed reads of the current one.
+    __shared__ __attribute__((aligned(16))) char K0[kTileBytes], V0[kTileBytes], K1[kTileBytes], V1[kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -760,30 +765,28 @@ void bwd_dq_kernel(const BwdParams p) {
     int n_kv = (N + BC - 1) / BC;
     if (CAUSAL) n_kv = (min(q0 + BRQ, N) - 1) / BC + 1;
 
-    constexpr int CPR = D / 8;
-    constexpr int PER = BC * CPR / NT;
-    static_assert(PER >= 1 && BC * CPR % NT == 0, "tile / threads mismatch");
-    u32x4 sk[PER], sv[PER];
-    auto load = [&](int kv0) {
+    // K/V tiles go straight from global memory into LDS (global_load_lds_dwordx4):
+    // one wave instruction fills 1 KiB, lane i writing bytes 16*i.., so lane i
+    // fetches the logical chunk that the swizzle assigns to its LDS slot.  Rows
+    // past the end are clamped to row N-1; their keys are masked (P = 0, dS = 0).
+    constexpr int RPI = 1024 / RB_D;               // tile rows per wave instruction
+    constexpr int CPR = RB_D / 16;                 // 16-byte chunks per row
+    constexpr int PERW = kTileBytes / 1024 / (NT / 64);
+    static_assert(PERW >= 1 && kTileBytes % (1024 * (NT / 64)) == 0, "tile / waves mismatch");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto load = [&](int kv0, FA2_LDS char* Ks, FA2_LDS char* Vs) {
+        const char* Kt = reinterpret_cast<const char*>(Kh + (size_t)kv0 * D);   // uniform tile bases
+        const char* Vt = reinterpret_cast<const char*>(Vh + (size_t)kv0 * D);
+        const int last = N - 1 - kv0;
+        int lr = lane / CPR, ls = lane % CPR;
+        asm volatile("" : "+v"(lr), "+v"(ls));   // rebuilt per tile instead of held across the loop
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR, col = (c % CPR) * 8;
-            sk[i] = u32x4{0, 0, 0, 0};
-            sv[i] = u32x4{0, 0, 0, 0};
-            if (kv0 + r < N) {
-                sk[i] = global_load16(Kh + (size_t)(kv0 + r) * D + col);
-                sv[i] = global_load16(Vh + (size_t)(kv0 + r) * D + col);
-            }
-        }
-    };
-    auto store = [&](FA2_LDS char* Ks, FA2_LDS char* Vs) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR, col = (c % CPR) * 8;
-            lds_store16(Ks + tile_off<RB_D>(r, col), sk[i]);
-            lds_store16(Vs + tile_off<RB_D>(r, col), sv[i]);
+        for (int i = 0; i < PERW; ++i) {
+            const int r = (wave_u * PERW + i) * RPI + lr;
+            const uint32_t off = (uint32_t)(min(r, last) * RB_D + 16 * (ls ^ swz<RB_D>(r)));
+            const int dst = (wave_u * PERW + i) * 1024;
+            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(Kt + off), (FA2_LDS void*)(Ks + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(Vt + off), (FA2_LDS void*)(Vs + dst), 16, 0, 0);
         }
     };
 
@@ -791,16 +794,10 @@ void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < NBD; ++i) acc[i] = zero16();
 
-    load(0);
-    store(smem, smem + kTileBytes);
-    __syncthreads();
-    for (int j = 0; j < n_kv; ++j) {
+    auto step = [&](int j, FA2_LDS char* Ks, FA2_LDS char* Vs, FA2_LDS char* Kn, FA2_LDS char* Vn)
+                    __attribute__((always_inline)) {
         const int kv0 = j * BC;
-        FA2_LDS char* Ks = smem + (j & 1) * (2 * kTileBytes);
-        FA2_LDS char* Vs = Ks + kTileBytes;
-        const bool has_next = j + 1 < n_kv;
-        if (has_next) load(kv0 + BC);
-
+        if (j + 1 < n_kv) load(kv0 + BC, Kn, Vn);   // the other buffer was released by the last barrier
         if (wave_live && !(CAUSAL && kv0 > wq0 + 31)) {
             const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
 #pragma unroll
@@ -835,11 +832,16 @@ void bwd_dq_kernel(const BwdParams p) {
                 }
             }
         }
-        if (has_next) {
-            FA2_LDS char* Kn = smem + ((j + 1) & 1) * (2 * kTileBytes);
-            store(Kn, Kn + kTileBytes);
-        }
-        __syncthreads();
+        wait_vm_all();             // the next tile has landed in LDS ...
+        __syncthreads();           // ... for every wave, and this one is free
+    };
+
+    load(0, (FA2_LDS char*)K0, (FA2_LDS char*)V0);
+    wait_vm_all();
+    __syncthreads();
+    for (int j = 0; j < n_kv; j += 2) {
+        step(j, (FA2_LDS char*)K0, (FA2_LDS char*)V0, (FA2_LDS char*)K1, (FA2_LDS char*)V1);
+        if (j + 1 < n_kv) step(j + 1, (FA2_LDS char*)K1, (FA2_LDS char*)V1, (FA2_LDS char*)K0, (FA2_LDS char*)V0);
     }
 
     if (wave_live && q < N) {

@@ -25,6 +25,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA2_LDS __attribute__((address_space(3)))
+#define FA2_GLOBAL __attribute__((address_space(1)))
 
 // Bit reinterpretation through by-value parameters.  Never apply
 // __builtin_bit_cast directly to an element of an ext_vector_type value
@@ -95,6 +96,10 @@ __device__ __forceinline__ bf16x8 cat_tr(s16x4 a, s16x4 b) {
     s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free).  The compiler does not
+// track loads that write LDS directly, so their consumers wait explicitly.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 __device__ __forceinline__ u32x4 global_load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);

@@ -53,15 +53,16 @@ constexpr int kThreads = 256;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
 
-// XOR swizzles of the 16-byte chunk index within an LDS row.
-//  K rows are read as 32 rows x 32 contiguous bytes per MFMA operand;
-//  V rows as 8 rows x 64 contiguous bytes per transposed read.
-template <int D> __device__ __forceinline__ int swz_k(int row) {
-    return D == 64 ? 2 * ((row >> 1) & 3) : 2 * (row & 7);
+// XOR swizzle of the 16-byte chunk index within an LDS row (rows of 2*D bytes).
+// The LDS serves 16-byte reads 16 lanes per clock and 8-byte reads 32 lanes
+// per clock over 64 banks.  K rows are read as 16 consecutive rows x one chunk
+// (MFMA row operands), V rows as 4 consecutive rows x 4 chunks (transposed
+// reads); this pattern puts both on 64 distinct banks.
+template <int D> __device__ __forceinline__ int swz(int row) {
+    return D == 64 ? 4 * ((row >> 1) & 1) + ((row >> 2) & 3) : 4 * (row & 3) + ((row >> 2) & 3);
 }
-template <int D> __device__ __forceinline__ int swz_v(int row) {
-    return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3);
-}
+template <int D> __device__ __forceinline__ int swz_k(int row) { return swz<D>(row); }
+template <int D> __device__ __forceinline__ int swz_v(int row) { return swz<D>(row); }
 
 template <int D, int BC>
 struct TileLoader {
