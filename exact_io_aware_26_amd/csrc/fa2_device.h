@@ -100,6 +100,22 @@ __device__ __forceinline__ bf16x8 cat_tr(s16x4 a, s16x4 b) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free).  The compiler does not
 // track loads that write LDS directly, so their consumers wait explicitly.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory operations done.
+template <int N> __device__ __forceinline__ void wait_vm_keep() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS reuse that leaves global->LDS copies in flight:
+// lgkmcnt(0), then s_barrier.  (A fenced barrier would also wait for every
+// outstanding copy, since the compiler counts them as pending LDS writes.)
+// Each wave waits for the copies that the next reads depend on with
+// wait_vm_keep / wait_vm_all before calling this.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("s_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ u32x4 global_load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);

@@ -288,13 +288,294 @@ void fwd_kernel(const FwdParams p) {
     }
 }
 
+// Pipelined forward for d = 64 and 128: one workgroup = 8 wave64s = 256 query
+// rows (two waves per SIMD), so each K/V tile brought into LDS serves twice
+// as many rows as a 4-wave workgroup would.
+//   * K/V tiles are copied from global memory straight into LDS
+//     (global_load_lds_dwordx4, no staging registers), three buffers deep, K
+//     one tile ahead of V: during step j the waves read K_{j+1} and V_j while
+//     K_{j+3} and V_{j+2} are in flight.  The six buffers are distinct LDS
+//     objects and the loop is unrolled by three, so no read names the buffer
+//     being filled and the compiler adds no wait on in-flight tiles; each step
+//     waits only for the copies issued one step earlier.
+//   * Within a wave the work is software-pipelined.  Step j runs the softmax
+//     of S_j (computed one step earlier) while the matrix cores compute
+//     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j while the row sums of
+//     P_j are added up, so vector and matrix work of neighbouring tiles
+//     overlap.
+//   * The running max m is raised only when a row's new max exceeds it by more
+//     than kLazyMax (log2 units).  O~, l and L all use the same m, so this is
+//     the same algebra as the method's rescale; it only bounds P by 2^kLazyMax
+//     instead of 1, and the O~ rescale becomes rare.
+constexpr float kLazyMax = 8.0f;
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fwd_pipe_kernel(const FwdParams p) {
+    constexpr int NW = 8, ROWS = 32 * NW, BC = 64;
+    constexpr int KSD = D / 16;          // MFMA reduction steps over the head dim
+    constexpr int NBD = D / 32;          // 32-wide blocks of the head dim (O^T)
+    constexpr int RB = 2 * D;            // bytes per LDS tile row
+    constexpr int kTile = BC * RB;
+    constexpr int RPI = 1024 / RB;       // tile rows per wave copy instruction
+    constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    constexpr int PERW = kTile / 1024 / NW;
+    static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile];
+    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile];
+    FA2_LDS char* const K0 = (FA2_LDS char*)Kb0;
+    FA2_LDS char* const K1 = (FA2_LDS char*)Kb1;
+    FA2_LDS char* const K2 = (FA2_LDS char*)Kb2;
+    FA2_LDS char* const V0 = (FA2_LDS char*)Vb0;
+    FA2_LDS char* const V1 = (FA2_LDS char*)Vb1;
+    FA2_LDS char* const V2 = (FA2_LDS char*)Vb2;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    const int BH = p.B * p.Hq;
+    const int level = blockIdx.x / BH;
+    const int bh = blockIdx.x - level * BH;
+    const int qtile = p.n_qtiles - 1 - level;
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hk = hq / p.G;
+    const int N = p.N;
+    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+    const uint16_t* Kh = p.K + khead;
+    const uint16_t* Vh = p.V + khead;
+
+    const int q0 = qtile * ROWS;
+    const int wq0 = q0 + 32 * wave;
+    const int q = wq0 + li;
+
+    bf16x8 qf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 v = {0, 0, 0, 0};
+        if (q < N) v = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
+        qf[ks] = as_bf16x8(v);
+    }
+
+    // Tiles the workgroup streams, and tiles this wave computes on.
+    const int n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
+    const int n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+
+    // Copy tile t of K or V into LDS.  Lane i of a copy instruction writes
+    // bytes 16*i.. of its 1 KiB (tile row R + i / CPR, 16-byte slot i % CPR),
+    // so it fetches the chunk the swizzle puts in that slot.  R is a multiple
+    // of RPI, and for these row strides swz(R + r) = swz(r) ^ swz(R) for
+    // r < RPI.  Rows past the end repeat row N-1 (their keys are masked).
+    auto copy_tile = [&](const uint16_t* head, int t, FA2_LDS char* dst) {
+        const int kv0 = t * BC;
+        const char* base = reinterpret_cast<const char*>(head + (size_t)kv0 * D);
+        const int last = N - 1 - kv0;
+        int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
+        asm volatile("" : "+v"(lr), "+v"(lc));   // rebuilt per tile instead of held across the loop
+#pragma unroll
+        for (int i = 0; i < PERW; ++i) {
+            const int R = (wave * PERW + i) * RPI;
+            const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<D>(R))));
+            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(base + off),
+                                             (FA2_LDS void*)(dst + (wave * PERW + i) * 1024), 16, 0, 0);
+        }
+    };
+
+    // The swizzle only flips bits 4.. of a row's byte offset below RB, so the
+    // operand addresses are a per-lane base XOR a constant: 32*ks for K rows
+    // (chunk 2*ks + g), 64*db for V columns.  The bases are rebuilt per step
+    // (opaque to the compiler) rather than holding one register per address.
+    auto scores = [&](const FA2_LDS char* Ks, f32x16 (&s)[2]) {
+        int kb = li * RB + 16 * (g ^ swz<D>(li));
+        asm volatile("" : "+v"(kb));
+        s[0] = zero16();
+        s[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int bs = 0; bs < 2; ++bs) {
+                const u32x4 a = lds_load16(Ks + 32 * bs * RB + (kb ^ (32 * ks)));
+                s[bs] = mfma32(as_bf16x8(a), qf[ks], s[bs]);
+            }
+    };
+
+    auto mask = [&](int t, f32x16 (&s)[2]) {
+        const int kv0 = t * BC;
+        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+#pragma unroll
+            for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
+                }
+        }
+    };
+
+    f32x16 o[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) o[i] = zero16();
+    float m_run = kNegInf;   // reference max of c * S (log2 domain), equal in lanes l and l ^ 32
+    float l_run = 0.f;       // this lane's half of the row sum, relative to m_run
+
+    // P = exp2(c S - m) in place (fp32, for the row sum) and packed to bf16
+    // (the B operand of the P V product); returns the rescale factor of O~ and l.
+    auto softmax = [&](f32x16 (&s)[2], uint32_t (&pp)[2][8]) -> float {
+        float mx = kNegInf;
+#pragma unroll
+        for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
+        mx = max_halves(mx) * p.c;
+        const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+        const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+#pragma unroll
+        for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
+                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
+                pp[bs][r >> 1] = pack_bf16(s[bs][r], s[bs][r + 1]);
+            }
+        return alpha;
+    };
+
+    auto row_sum = [&](const f32x16 (&pr)[2], float alpha) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) lsum += pr[bs][r] + pr[bs][r + 1];
+        l_run = fmaf(l_run, alpha, lsum);
+    };
+
+    // O^T += V^T P^T: V^T fragments by transposed reads of the row-major V tile
+    // (rows 16*kk + 4*g + j16/4 and +8, columns 32*db + 16*half + 4*(j16 % 4)).
+    auto pv = [&](const FA2_LDS char* Vs, const uint32_t (&pp)[2][8]) {
+        const int j16 = lane & 15;
+        const int x = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);    // chunk within a 32-column block
+        const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+        int vb1 = r1 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r1));
+        int vb2 = r2 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r2));
+        asm volatile("" : "+v"(vb1), "+v"(vb2));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int bs = kk >> 1, h = kk & 1;
+            const bf16x8 bfrag = as_bf16x8(u32x4{pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2], pp[bs][4 * h + 3]});
+#pragma unroll
+            for (int db = 0; db < NBD; ++db) {
+                const s16x4 t1 = lds_load_tr(Vs + 16 * kk * RB + (vb1 ^ (64 * db)));
+                const s16x4 t2 = lds_load_tr(Vs + 16 * kk * RB + (vb2 ^ (64 * db)));
+                o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
+            }
+        }
+    };
+
+    // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
+    copy_tile(Kh, 0, K0);
+    copy_tile(Vh, 0, V0);
+    if (1 < n_kv) {
+        copy_tile(Kh, 1, K1);
+        copy_tile(Vh, 1, V1);
+    }
+    if (2 < n_kv) copy_tile(Kh, 2, K2);
+    wait_vm_all();
+    __syncthreads();
+    f32x16 sa[2], sb[2];       // scores of the current and the next tile, alternating
+    scores(K0, sa);
+    __syncthreads();          // K_0 is overwritten by K_3 in step 0
+
+    // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
+    // then P_j V_j.  Past a wave's last tile the step only copies; S_{j+1} of a
+    // tile the wave does not visit is computed from whatever its buffer holds
+    // and never used.
+    auto step = [&](int j, const FA2_LDS char* Ks, const FA2_LDS char* Vs, FA2_LDS char* Kw, FA2_LDS char* Vw,
+                    f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
+        // Copies past the last tile repeat it into a released buffer that is
+        // never read, so every step issues and waits for the same count.
+        copy_tile(Kh, min(j + 3, n_kv - 1), Kw);
+        copy_tile(Vh, min(j + 2, n_kv - 1), Vw);
+        if (j < n_w) {
+            mask(j, s_cur);
+            uint32_t pp[2][8];
+            scores(Ks, s_next);
+            const float alpha = softmax(s_cur, pp);
+            // Materialize P here, beside the S_{j+1} products, rather than
+            // letting the compiler sink the exponentials below the branch.
+#pragma unroll
+            for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int i = 0; i < NBD; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
+            pv(Vs, pp);
+            row_sum(s_cur, alpha);
+        }
+        wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
+        barrier_lds();
+    };
+
+    // Unrolled by six: three buffer phases times two score arrays.
+    for (int j = 0; j < n_kv; j += 6) {
+        step(j, K1, V0, K0, V2, sa, sb);
+        if (j + 1 >= n_kv) break;
+        step(j + 1, K2, V1, K1, V0, sb, sa);
+        if (j + 2 >= n_kv) break;
+        step(j + 2, K0, V2, K2, V1, sa, sb);
+        if (j + 3 >= n_kv) break;
+        step(j + 3, K1, V0, K0, V2, sb, sa);
+        if (j + 4 >= n_kv) break;
+        step(j + 4, K2, V1, K1, V0, sa, sb);
+        if (j + 5 >= n_kv) break;
+        step(j + 5, K0, V2, K2, V1, sb, sa);
+    }
+    wait_vm_all();
+
+    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l)
+    if (n_w > 0) {
+        const float l_tot = sum_halves(l_run);
+        const float inv = 1.0f / l_tot;
+        if (q < N) {
+            uint16_t* Orow = p.O + qhead + (size_t)q * D;
+#pragma unroll
+            for (int db = 0; db < NBD; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * db + 8 * rq + 4 * g;
+                    u32x2 w;
+                    w[0] = pack_bf16(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+                    w[1] = pack_bf16(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
+                }
+            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-    const long grid = (long)p.B * p.Hq * p.n_qtiles;
     FwdParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, CAUSAL>),
-                           dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+    if constexpr (D <= 128) {
+        arg.n_qtiles = (p.N + 255) / 256;
+        const long grid = (long)p.B * p.Hq * arg.n_qtiles;
+        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL>),
+                               dim3((unsigned)grid), dim3(512), args, 0, stream);
+    } else {
+        arg.n_qtiles = (p.N + kFwdRows - 1) / kFwdRows;
+        const long grid = (long)p.B * p.Hq * arg.n_qtiles;
+        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, CAUSAL>),
+                               dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+    }
 }
 
 }  // namespace
