@@ -19,6 +19,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip"]
+# Per-source code generation options.  The backward kernels feed matrix-core
+# results straight into vector arithmetic; with this option the compiler keeps
+# those results in ordinary VGPRs instead of accumulation registers that would
+# have to be copied out first.
+SOURCE_FLAGS = {"fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 FLAGS = [
@@ -38,7 +43,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is expected.
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -56,7 +56,12 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 
 struct Sizes {
     uint64_t q_elems = 0, kv_elems = 0, rows = 0;  // rows = B * Hq * N
+    uint64_t rows_pad = 0;                          // B * Hq * N rounded up per head
 };
+
+// Rows of the per-row workspace arrays of one head: N rounded up to a
+// multiple of kBwdRowPad.
+int padded_rows(int N) { return (N + fa2::kBwdRowPad - 1) / fa2::kBwdRowPad * fa2::kBwdRowPad; }
 
 // Shared checks of sizes, head dim, scale and grid limits.  Returns FA2_OK
 // with *empty set when there is nothing to compute.
@@ -79,6 +84,8 @@ fa2_status check_problem(int B, int Hq, int Hkv, int N, int d, float scale, bool
         !count4(B, Hq, N, 1, &sz->rows) || sz->q_elems > (UINT64_MAX >> 3))
         return fail(FA2_ERR_INVALID_ARGUMENT, "element count overflows 64 bits");
     if (N > kMaxN) return fail(FA2_ERR_UNSUPPORTED, "N above 2^30");
+    if (!count4(B, Hq, padded_rows(N), 1, &sz->rows_pad) || sz->rows_pad > (UINT64_MAX >> 4))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "element count overflows 64 bits");
     // Largest grid launched: forward B*Hq*ceil(N/128) or backward B*Hkv*ceil(N/64), 256 threads.
     const uint64_t tiles = (uint64_t)B * (uint64_t)Hq * (uint64_t)((N + 63) / 64);
     if (tiles * 256u > kMaxGridThreads) return fail(FA2_ERR_UNSUPPORTED, "grid too large");
@@ -105,13 +112,16 @@ fa2_status validate_fwd(const void* Q, const void* K, const void* V, const void*
 }
 
 struct WorkspaceLayout {
-    size_t d_off, dq_off, total;
+    size_t d_off, l2_off, dq_off, total;
 };
 
-WorkspaceLayout workspace_layout(uint64_t rows, uint64_t q_elems) {
+// D [B*Hq*Npad] fp32, then L * log2(e) [B*Hq*Npad] fp32, then the dQ
+// accumulator [B*Hq*N*d] fp32, each on a 256-byte boundary.
+WorkspaceLayout workspace_layout(uint64_t rows_pad, uint64_t q_elems) {
     WorkspaceLayout w;
     w.d_off = 0;
-    w.dq_off = align_up(rows * 4, kWorkspaceAlign);
+    w.l2_off = align_up(rows_pad * 4, kWorkspaceAlign);
+    w.dq_off = w.l2_off + align_up(rows_pad * 4, kWorkspaceAlign);
     w.total = w.dq_off + align_up(q_elems * 4, kWorkspaceAlign);
     return w;
 }
@@ -131,7 +141,7 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
     if (!ws) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) != 0)
         return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    const WorkspaceLayout wl = workspace_layout(sz->rows, sz->q_elems);
+    const WorkspaceLayout wl = workspace_layout(sz->rows_pad, sz->q_elems);
     if (ws_bytes < wl.total) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace too small");
     const uint64_t qb = sz->q_elems * 2, kb = sz->kv_elems * 2, lb = sz->rows * 4;
     const void* ins[6] = {Q, K, V, O, L, dO};
@@ -194,11 +204,11 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
     if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return 0;
     if (B == 0 || Hq == 0 || N == 0) return 0;
     if (Hkv < 1 || Hq % Hkv != 0) return 0;
-    uint64_t q_elems, rows;
-    if (!count4(B, Hq, N, d, &q_elems) || !count4(B, Hq, N, 1, &rows) ||
-        q_elems > (UINT64_MAX >> 3))
+    uint64_t q_elems, rows_pad;
+    if (N > kMaxN || !count4(B, Hq, N, d, &q_elems) || !count4(B, Hq, padded_rows(N), 1, &rows_pad) ||
+        q_elems > (UINT64_MAX >> 3) || rows_pad > (UINT64_MAX >> 4))
         return 0;
-    return workspace_layout(rows, q_elems).total;
+    return workspace_layout(rows_pad, q_elems).total;
 }
 
 fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq,
@@ -247,7 +257,7 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
     fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
                                 Hkv, N, d, scale, &empty, &sz);
     if (s != FA2_OK || empty) return s;
-    const WorkspaceLayout wl = workspace_layout(sz.rows, sz.q_elems);
+    const WorkspaceLayout wl = workspace_layout(sz.rows_pad, sz.q_elems);
     fa2::BwdParams p;
     p.Q = static_cast<const uint16_t*>(Q);
     p.K = static_cast<const uint16_t*>(K);
@@ -259,11 +269,13 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
     p.dK = static_cast<uint16_t*>(dK);
     p.dV = static_cast<uint16_t*>(dV);
     p.Dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.d_off);
+    p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.l2_off);
     p.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off);
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.N = N;
+    p.Npad = padded_rows(N);
     p.G = Hq / Hkv;
     p.scale = scale;
     p.c = (float)((double)scale * kLog2e);

@@ -91,16 +91,21 @@ template <> struct BwdCfg<128> { static constexpr int BC = 128, NW = 4, BR = 64;
 template <> struct BwdCfg<256> { static constexpr int BC = 64, NW = 2, BR = 32; static constexpr bool KV_REGS = false; };
 
 // ---------------------------------------------------------------------------------------------
-// bwd_pre: D_i = sum_d dO_id * O_id (fp32); zero the dQ accumulator row when dQ
-// is accumulated with atomics.
+// bwd_pre: per padded row of each head, D_i = sum_d dO_id * O_id (fp32) and
+// L_i * log2(e); rows past N get D = 0 and +inf (so P = 0 there).  Zeroes the
+// dQ accumulator row when dQ is accumulated with atomics.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long rows, int zero_dq) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long rows_pad, int zero_dq) {
     constexpr int LPR = D / 8;                 // lanes per row (8 bf16 each)
     constexpr int RPB = 256 / LPR;             // rows per block
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const long rp = (long)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
+    const long bh = rp / p.Npad;
+    const int qi = (int)(rp - bh * p.Npad);
+    const bool valid = rp < rows_pad && qi < p.N;
+    const long row = bh * p.N + qi;            // unpadded row (valid rows only)
     float acc = 0.f;
-    if (row < rows) {
+    if (valid) {
         const size_t off = (size_t)row * D + part * 8;
         const u32x4 a = global_load16(p.dO + off);
         const u32x4 b = global_load16(p.O + off);
@@ -118,7 +123,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-    if (row < rows && part == 0) p.Dsum[row] = acc;
+    if (rp < rows_pad && part == 0) {
+        p.Dsum[rp] = acc;
+        p.L2[rp] = valid ? p.L[row] * kLog2e : kInf;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -252,8 +260,8 @@ void bwd_main_kernel(const BwdParams p) {
         if (tid < BR) {
             // Raw values from a clamped row; scaled and masked when written to LDS,
             // so nothing here waits for these loads to land.
-            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)N + min(qt0 + tid, N - 1);
-            sl = p.L[r];
+            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(qt0 + tid, N - 1);
+            sl = p.L2[r];
             sd = p.Dsum[r];
         }
     };
@@ -325,7 +333,7 @@ void bwd_main_kernel(const BwdParams p) {
         }
         if (tid < BR) {
             const bool in = qt0 + tid < N;
-            Ls[tid] = in ? sl * kLog2e : kInf;         // rows past the end get P = 0
+            Ls[tid] = in ? sl : kInf;                  // rows past the end get P = 0
             Dl[tid] = in ? sd : 0.f;
         }
         __syncthreads();                               // (A) tile visible
@@ -544,8 +552,8 @@ void bwd_pair_kernel(const BwdParams p) {
             }
         }
         if (tid < BR) {   // raw values from a clamped row; scaled and masked when stored
-            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)N + min(qt0 + tid, N - 1);
-            sl = p.L[r];
+            const size_t r = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(qt0 + tid, N - 1);
+            sl = p.L2[r];
             sd = p.Dsum[r];
         }
     };
@@ -605,7 +613,7 @@ void bwd_pair_kernel(const BwdParams p) {
         }
         if (tid < BR) {
             const bool in = qt0 + tid < N;
-            Ls[tid] = in ? sl * kLog2e : kInf;   // rows past the end get P = 0
+            Ls[tid] = in ? sl : kInf;   // rows past the end get P = 0
             Dl[tid] = in ? sd : 0.f;
         }
         __syncthreads();                         // (A)
@@ -758,8 +766,8 @@ void bwd_dq_kernel(const BwdParams p) {
         qf[ks] = as_bf16x8(a);
         of[ks] = as_bf16x8(c);
     }
-    const size_t row = ((size_t)b * p.Hq + hq) * (size_t)N + min(q, N - 1);
-    const float l2 = q < N ? p.L[row] * kLog2e : kInf;   // rows past the end: P = 0
+    const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
+    const float l2 = q < N ? p.L2[row] : kInf;   // rows past the end: P = 0
     const float dq_d = q < N ? p.Dsum[row] : 0.f;
 
     int n_kv = (N + BC - 1) / BC;
@@ -785,8 +793,8 @@ void bwd_dq_kernel(const BwdParams p) {
             const int r = (wave_u * PERW + i) * RPI + lr;
             const uint32_t off = (uint32_t)(min(r, last) * RB_D + 16 * (ls ^ swz<RB_D>(r)));
             const int dst = (wave_u * PERW + i) * 1024;
-            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(Kt + off), (FA2_LDS void*)(Ks + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(Vt + off), (FA2_LDS void*)(Vs + dst), 16, 0, 0);
+            copy_to_lds16(Kt, off, Ks + dst);
+            copy_to_lds16(Vt, off, Vs + dst);
         }
     };
 
@@ -859,6 +867,292 @@ void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// bwd_kv: the K/V-tile loop for d = 64 and 128 (dQ in its own pass).
+//
+// One workgroup = 4 wave64s = 128 keys; wave w owns keys 32w..32w+31 and the
+// whole head dim of their dK and dV, accumulated in registers (one wave per
+// SIMD with the full register file).  Query tiles of 64 rows -- Q, dO, and
+// the L log2(e) and D rows of the workspace -- are copied into LDS with
+// global_load_lds, three tiles deep, in nine distinct LDS arrays with the loop
+// unrolled by three (no read names a buffer in flight; each step waits only
+// for the copies issued one step earlier).  Per 32-row query block every
+// product is arranged so that each lane owns one key:
+//     s  = Q K^T,  dp = dO V^T     A: Q / dO rows from LDS, B: this lane's K / V row
+//     P  = exp2(c s - L log2 e),   dS = P o (dp - D)      (masked on the diagonal)
+//     dV^T += dO^T P,  dK^T += Q^T dS
+//                                  A: dO^T / Q^T by transposed LDS reads,
+//                                  B: P / dS straight from the s / dp registers,
+// since a score accumulator register holds the 8 queries, in the order of the
+// transposed reads, that the B operand of a 16-query step needs.  Within a
+// tile, the vector work of one query block overlaps the products of the other.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_kv_kernel(const BwdParams p) {
+    constexpr int NW = 4, BC = 32 * NW, BR = kBwdRowPad;
+    constexpr int RB = 2 * D;                 // bytes per row of the Q / dO tiles
+    constexpr int kTile = BR * RB;
+    constexpr int KSD = D / 16;               // reduction steps over the head dim
+    constexpr int NBD = D / 32;               // 32-wide head-dim blocks
+    constexpr int RPI = 1024 / RB;            // tile rows per wave copy instruction
+    constexpr int CPR = RB / 16;              // 16-byte chunks per row
+    constexpr int PERW = kTile / 1024 / NW;   // copy instructions per wave per tensor
+    static_assert(BR == 64 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    __shared__ __attribute__((aligned(16))) char Qa0[kTile], Qa1[kTile], Qa2[kTile];
+    __shared__ __attribute__((aligned(16))) char Oa0[kTile], Oa1[kTile], Oa2[kTile];
+    __shared__ __attribute__((aligned(16))) float La0[2 * BR], La1[2 * BR], La2[2 * BR];   // [L log2 e | D]
+    FA2_LDS char* const Q0 = (FA2_LDS char*)Qa0;
+    FA2_LDS char* const Q1 = (FA2_LDS char*)Qa1;
+    FA2_LDS char* const Q2 = (FA2_LDS char*)Qa2;
+    FA2_LDS char* const O0 = (FA2_LDS char*)Oa0;
+    FA2_LDS char* const O1 = (FA2_LDS char*)Oa1;
+    FA2_LDS char* const O2 = (FA2_LDS char*)Oa2;
+    FA2_LDS float* const L0 = (FA2_LDS float*)La0;
+    FA2_LDS float* const L1 = (FA2_LDS float*)La1;
+    FA2_LDS float* const L2b = (FA2_LDS float*)La2;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    const int BHk = p.B * p.Hkv;
+    const int kvtile = blockIdx.x / BHk;
+    const int bh = blockIdx.x - kvtile * BHk;
+    const int b = bh / p.Hkv;
+    const int hk = bh - b * p.Hkv;
+    const int N = p.N;
+    const int kv0 = kvtile * BC;
+    const int kw0 = kv0 + 32 * wave;
+    const int kv = kw0 + li;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+
+    bf16x8 kf[KSD], vf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+        if (kv < N) {
+            kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
+            vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
+        }
+        kf[ks] = as_bf16x8(kx);
+        vf[ks] = as_bf16x8(vx);
+    }
+    f32x16 dv[NBD], dk[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) {
+        dv[i] = zero16();
+        dk[i] = zero16();
+    }
+
+    // Query tiles: for each of the G query heads sharing this K/V head, the
+    // 64-row tiles from the first one the causal mask lets through.
+    const int n_qt = (N + BR - 1) / BR;
+    const int i_begin = CAUSAL ? kv0 / BR : 0;
+    const int n_i = n_qt - i_begin;
+    const int n_iter = n_i * p.G;
+
+    // Copy query tile `it` into LDS: Q and dO rows (clamped to N-1 past the
+    // end; those rows have L = +inf, so P = dS = 0), and the padded L log2 e
+    // and D rows (waves 0 and 2 both copy L, 1 and 3 both copy D: identical
+    // bytes, so every wave issues the same number of copies).
+    auto copy_tile = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
+        const int hq = hk * p.G + it / n_i;
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
+        const char* qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
+        const char* obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
+        const int last = N - 1 - qt0;
+        int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
+        asm volatile("" : "+v"(lr), "+v"(lc));   // rebuilt per tile instead of held across the loop
+#pragma unroll
+        for (int i = 0; i < PERW; ++i) {
+            const int R = (wave * PERW + i) * RPI;
+            const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<RB>(R))));
+            copy_to_lds16(qbase, off, Qd + (wave * PERW + i) * 1024);
+            copy_to_lds16(obase, off, Od + (wave * PERW + i) * 1024);
+        }
+        const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
+        const float* src = (wave & 1) ? p.Dsum + prow : p.L2 + prow;
+        copy_to_lds4(src, 4 * lane, Ld + (wave & 1) * BR);
+    };
+
+    // LDS operand addresses: the swizzle only flips bits 4.. of a row's byte
+    // offset below RB, so they are a per-lane base XOR a constant (32*ks for
+    // Q / dO rows, chunk 2*ks + g; 64*db for the transposed reads).
+    const int j16 = lane & 15;
+    const int xq = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+    const int kb_lane = li * RB + 16 * (g ^ swz<RB>(li));
+    const int vb1_lane = r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1));
+    const int vb2_lane = r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2));
+
+    // One query tile as a fixed program of matrix products, one per slot
+    // (NS = 2 * D/16 products of s and dp per 32-row block, NG = 4 * D/32 of
+    // dV and dK; 16, 16 for d = 128):
+    //   s, dp of block 0          (A: Q / dO rows, B: K / V of this lane)
+    //   s, dp of block 1          | P, dS of block 0, 16 / NS elements per slot
+    //   dV, dK over block 0       | P, dS of block 1, 16 / NG elements per slot
+    //   dV, dK over block 1
+    // Each product's A operand is read from LDS kPrefetch slots ahead; a
+    // scheduling fence between slots keeps this order, so the compiler waits
+    // only for the read a product needs.
+    constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = 2 * NS + 2 * NG;
+    constexpr int kPrefetch = 4;
+    static_assert(16 % NS == 0 && 16 % NG == 0 && NS >= 8, "slot program shape");
+    auto tile = [&](const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls, int qt0) {
+        int kb = kb_lane, vb1 = vb1_lane, vb2 = vb2_lane;
+        asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2));   // rebuilt per tile, not held across the loop
+        f32x16 sc[2], dpc[2];
+        uint32_t pp[2][8], pd[2][8];
+        f32x4 lv[2][4], dd[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            sc[i] = zero16();
+            dpc[i] = zero16();
+        }
+        // A operand of product k.
+        auto load_a = [&](int k) -> bf16x8 {
+            if (k < 2 * NS) {
+                const int blk = k / NS, ks = (k % NS) >> 1;
+                const FA2_LDS char* t = (k & 1) ? Os : Qs;
+                return as_bf16x8(lds_load16(t + 32 * blk * RB + (kb ^ (32 * ks))));
+            }
+            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            const FA2_LDS char* t = (jj & 1) ? Qs : Os;
+            const int base = 16 * (2 * blk + h) * RB;
+            return cat_tr(lds_load_tr(t + base + (vb1 ^ (64 * db))), lds_load_tr(t + base + (vb2 ^ (64 * db))));
+        };
+        auto product = [&](int k, bf16x8 a) {
+            if (k < 2 * NS) {
+                const int blk = k / NS, ks = (k % NS) >> 1;
+                if (k & 1) dpc[blk] = mfma32(a, vf[ks], dpc[blk]);
+                else sc[blk] = mfma32(a, kf[ks], sc[blk]);
+                return;
+            }
+            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            if (jj & 1) {
+                const bf16x8 bs = as_bf16x8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
+                dk[db] = mfma32(a, bs, dk[db]);
+            } else {
+                const bf16x8 bp = as_bf16x8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
+                dv[db] = mfma32(a, bp, dv[db]);
+            }
+        };
+        // Element r of P and dS of block blk (query 8*(r/4) + 4g + r%4 of the
+        // block, this lane's key).
+        auto element = [&](int blk, int r) {
+            const int rq = r >> 2, e = r & 3;
+            const float pr = exp2_fast(fmaf(sc[blk][r], p.c, -lv[blk][rq][e]));
+            const float ds = pr * (dpc[blk][r] - dd[blk][rq][e]);
+            sc[blk][r] = pr;                 // the fp32 values are kept until their pair is packed
+            dpc[blk][r] = ds;
+            if (r & 1) {
+                pp[blk][r >> 1] = pack_bf16(sc[blk][r - 1], pr);
+                pd[blk][r >> 1] = pack_bf16(dpc[blk][r - 1], ds);
+            }
+        };
+        // Vector work of slot k: L and D of a block are read half a block of
+        // products before its P, dS; then the elements.
+        auto vector_work = [&](int k) {
+            const int rl = k - NS / 2;                        // block 0 reads: slots NS/2 .. NS/2+3
+            if (rl >= 0 && rl < 4) {
+                const int ql = 8 * rl + 4 * g;
+                lv[0][rl] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
+                dd[0][rl] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + BR + ql);
+            }
+            const int rl1 = k - (NS + NS / 2);                // block 1 reads
+            if (rl1 >= 0 && rl1 < 4) {
+                const int ql = 32 + 8 * rl1 + 4 * g;
+                lv[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
+                dd[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + BR + ql);
+            }
+            if (k >= NS && k < 2 * NS) {
+                constexpr int E = 16 / NS;
+#pragma unroll
+                for (int i = 0; i < E; ++i) element(0, (k - NS) * E + i);
+            } else if (k >= 2 * NS && k < 2 * NS + NG) {
+                constexpr int E = 16 / NG;
+#pragma unroll
+                for (int i = 0; i < E; ++i) element(1, (k - 2 * NS) * E + i);
+            }
+        };
+        // Causal mask of block blk, once its scores are complete: only a block
+        // that starts below this wave's last key has keys above the diagonal
+        // (one or two blocks per query head in a wave's whole loop).
+        auto mask = [&](int blk) {
+            if (CAUSAL && qt0 + 32 * blk < kw0 + 31) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk][i] = -kInf;
+            }
+        };
+        bf16x8 abuf[kPrefetch];
+        auto slot = [&](int k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 a = abuf[k % kPrefetch];
+            if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
+            product(k, a);
+            vector_work(k);
+        };
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) slot(k);
+        mask(0);
+#pragma unroll
+        for (int k = NS; k < 2 * NS; ++k) slot(k);
+        mask(1);
+#pragma unroll
+        for (int k = 2 * NS; k < NP; ++k) slot(k);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto step = [&](int it, const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls,
+                    FA2_LDS char* Qw, FA2_LDS char* Ow, FA2_LDS float* Lw) __attribute__((always_inline)) {
+        // Copies past the last tile repeat it into a released buffer that is
+        // never read, so every step issues and waits for the same count.
+        copy_tile(min(it + 2, n_iter - 1), Qw, Ow, Lw);
+        tile(Qs, Os, Ls, (i_begin + it % n_i) * BR);
+        wait_vm_keep<2 * PERW + 1>();   // tile it+1, issued one step earlier, has landed
+        barrier_lds();
+    };
+
+    if (n_iter > 0) {
+        copy_tile(0, Q0, O0, L0);
+        if (n_iter > 1) copy_tile(1, Q1, O1, L1);
+        wait_vm_all();
+        __syncthreads();
+        for (int it = 0; it < n_iter; it += 3) {
+            step(it, Q0, O0, L0, Q2, O2, L2b);
+            if (it + 1 < n_iter) {
+                step(it + 1, Q1, O1, L1, Q0, O0, L0);
+                if (it + 2 < n_iter) step(it + 2, Q2, O2, L2b, Q1, O1, L1);
+            }
+        }
+        wait_vm_all();
+    }
+
+    // epilogue: this lane's key, the whole head dim
+    if (kv < N) {
+        uint16_t* dVr = p.dV + khead + (size_t)kv * D;
+        uint16_t* dKr = p.dK + khead + (size_t)kv * D;
+#pragma unroll
+        for (int db = 0; db < NBD; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d0 = 32 * db + 8 * rq + 4 * g;
+                *reinterpret_cast<u32x2*>(dVr + d0) =
+                    u32x2{pack_bf16(dv[db][4 * rq], dv[db][4 * rq + 1]),
+                          pack_bf16(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
+                *reinterpret_cast<u32x2*>(dKr + d0) =
+                    u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
+                          pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // dQ = bf16(scale * accumulator), 8 elements per thread.
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const BwdParams p, long n8) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -878,14 +1172,15 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream) {
     BwdParams arg = p;
     const long rows = (long)p.B * p.Hq * p.N;
+    const long rows_pad = (long)p.B * p.Hq * p.Npad;
     const bool atomic_dq = (stages & 8u) != 0;
     if (stages & 1u) {
         constexpr int RPB = 256 / (D / 8);
-        long rows_arg = rows;
+        long rows_arg = rows_pad;
         int zero = atomic_dq ? 1 : 0;
         void* args[] = {&arg, &rows_arg, &zero};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_pre_kernel<D>),
-                                       dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), args, 0, stream);
+                                       dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
     if (stages & 2u) {
@@ -894,10 +1189,14 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
         long grid;
         unsigned threads;
         if constexpr (D <= 128) {
-            fn = atomic_dq ? reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>)
-                           : reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, false>);
+            if (atomic_dq) {
+                fn = reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>);
+                threads = 512;
+            } else {
+                fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL>);
+                threads = 256;
+            }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
-            threads = 512;
         } else {
             fn = atomic_dq ? reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>)
                            : reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, false>);

@@ -97,13 +97,32 @@ __device__ __forceinline__ bf16x8 cat_tr(s16x4 a, s16x4 b) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free).  The compiler does not
-// track loads that write LDS directly, so their consumers wait explicitly.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// s_waitcnt vmcnt(N): all but the N most recent vector-memory operations done.
+// Asynchronous copies from global memory into LDS (global_load_lds_*): lane i
+// of the wave writes its bytes at lds + SIZE*i, read from gbase + voff (gbase
+// and lds wave-uniform, voff per lane).  They are issued as inline assembly:
+// the compiler's own wait insertion then treats in-flight copies as unknown,
+// instead of draining every outstanding LDS read (lgkmcnt(0)) before each use
+// as it does for the builtin.  The copies count in vmcnt only (measured on
+// gfx950: an in-flight copy does not hold lgkmcnt), so readers wait with
+// wait_vm_keep / wait_vm_all followed by a barrier.  Nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void copy_to_lds16(const void* gbase, uint32_t voff, const FA2_LDS void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+__device__ __forceinline__ void copy_to_lds4(const void* gbase, uint32_t voff, const FA2_LDS void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 ::"s"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+
+// s_waitcnt vmcnt(0) / vmcnt(N): all / all but the N most recent vector-memory
+// operations (including the copies above) done.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 template <int N> __device__ __forceinline__ void wait_vm_keep() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier for LDS reuse that leaves global->LDS copies in flight:

@@ -380,8 +380,7 @@ void fwd_pipe_kernel(const FwdParams p) {
         for (int i = 0; i < PERW; ++i) {
             const int R = (wave * PERW + i) * RPI;
             const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<D>(R))));
-            __builtin_amdgcn_global_load_lds((FA2_GLOBAL void*)(base + off),
-                                             (FA2_LDS void*)(dst + (wave * PERW + i) * 1024), 16, 0, 0);
+            copy_to_lds16(base, off, dst + (wave * PERW + i) * 1024);
         }
     };
 

@@ -26,12 +26,18 @@ struct BwdParams {
     uint16_t* dQ;
     uint16_t* dK;
     uint16_t* dV;
-    float* Dsum;   // fp32 [B, Hq, N]     workspace: D = rowsum(dO o O)
+    float* Dsum;   // fp32 [B, Hq, Npad]  workspace: D = rowsum(dO o O); 0 past N
+    float* L2;     // fp32 [B, Hq, Npad]  workspace: L * log2(e); +inf past N (P = 0 there)
     float* dQacc;  // fp32 [B, Hq, N, D]  workspace: dQ accumulated with atomics
     int B, Hq, Hkv, N, G;
+    int Npad;      // N rounded up to a multiple of kBwdRowPad
     float scale;
     float c;       // scale * log2(e)
 };
+
+// Row padding of the backward's per-row workspace arrays (one query tile of
+// the K/V-tile loop), so that whole tiles of L and D can be copied unchecked.
+constexpr int kBwdRowPad = 64;
 
 // Rows of Q per forward workgroup (the grid is B * Hq * ceil(N / kFwdRows)).
 constexpr int kFwdRows = 128;

@@ -84,10 +84,12 @@ fa2_status fa2_fwd(const void *Q, const void *K, const void *V, void *O, float *
                    void *stream);
 
 /*
- * Bytes of device workspace fa2_bwd needs: an fp32 [B,Hq,N] array for
- * D = rowsum(dO o O) and an fp32 [B,Hq,N,d] array accumulating dQ, each
- * starting on a 256-byte boundary.  Returns 0 for an empty problem and for
- * invalid sizes (negative, or Hq % Hkv != 0).
+ * Bytes of device workspace fa2_bwd needs: two fp32 [B,Hq,Npad] arrays
+ * (Npad = N rounded up to a multiple of 64) holding D = rowsum(dO o O) and
+ * L * log2(e) per query row, and an fp32 [B,Hq,N,d] array accumulating dQ in
+ * the atomic mode, each starting on a 256-byte boundary.  Returns 0 for an
+ * empty problem and for sizes fa2_bwd rejects (negative, Hq % Hkv != 0,
+ * N above 2^30, byte counts that overflow).
  */
 size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
@@ -99,7 +101,7 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *   summed over the Hq/Hkv query heads sharing each key/value head).
  *   workspace: caller-allocated device memory, 256-byte aligned, of at least
  *   fa2_bwd_workspace_bytes(...) bytes; contents undefined on entry and exit.
- *   (The default path uses only its D part; the atomic mode of
+ *   (The default path uses only its two per-row arrays; the atomic mode of
  *   fa2_bwd_stages also uses the dQ accumulator.)
  * Errors: as fa2_fwd, plus FA2_ERR_INVALID_ARGUMENT when the workspace is
  * NULL, misaligned or too small, or when an output aliases an input or
@@ -115,7 +117,8 @@ fa2_status fa2_bwd(const void *Q, const void *K, const void *V, const void *O,
  * The backward pass as its three launches, selected by a bit mask, with the
  * same arguments and checks as fa2_bwd:
  *   FA2_BWD_PREPROCESS  D = rowsum(dO o O) (section 4 symbol table of the
- *                       FlashAttention-2 summary page) into the workspace;
+ *                       FlashAttention-2 summary page) and L * log2(e)
+ *                       into the workspace;
  *   FA2_BWD_MAIN        the loop over K/V tiles that writes dK and dV
  *                       (same page, section 2: the backward's outer loop runs
  *                       over K/V column blocks);

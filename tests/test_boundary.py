@@ -142,9 +142,10 @@ def test_workspace_size(lib):
     B, Hq, Hkv, N, d = 2, 4, 2, 100, 128
     need = ws_bytes(lib)
     rows = B * Hq * N
+    rows_pad = B * Hq * ((N + 63) // 64 * 64)   # per-row arrays padded to 64 rows per head
     def up(x):
         return (x + 255) // 256 * 256
-    assert need == up(rows * 4) + up(rows * d * 4)
+    assert need == 2 * up(rows_pad * 4) + up(rows * d * 4)
     assert vbwd(lib, ws=need - 1) == INVALID
     assert b"workspace" in lib.fa2_last_error()
     assert vbwd(lib, ws=need + 12345) == OK
