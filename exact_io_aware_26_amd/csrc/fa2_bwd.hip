@@ -1040,20 +1040,22 @@ void bwd_kv_kernel(const BwdParams p) {
             }
         };
         // Element r of P and dS of block blk (query 8*(r/4) + 4g + r%4 of the
-        // block, this lane's key).
-        auto element = [&](int blk, int r) {
-            const int rq = r >> 2, e = r & 3;
-            const float pr = exp2_fast(fmaf(sc[blk][r], p.c, -lv[blk][rq][e]));
-            const float ds = pr * (dpc[blk][r] - dd[blk][rq][e]);
-            sc[blk][r] = pr;                 // the fp32 values are kept until their pair is packed
-            dpc[blk][r] = ds;
+        // block, this lane's key) in three stages -- c*s - L log2 e, exp2, then
+        // dS and the bf16 packing -- run for elements r, r-1, r-2 in one slot,
+        // so the instructions of a slot do not wait on each other.
+        auto stage_a = [&](int blk, int r) { sc[blk][r] = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]); };
+        auto stage_b = [&](int blk, int r) { sc[blk][r] = exp2_fast(sc[blk][r]); };
+        auto stage_c = [&](int blk, int r) {
+            const float pr = sc[blk][r];
+            const float ds = pr * (dpc[blk][r] - dd[blk][r >> 2][r & 3]);
+            dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
             if (r & 1) {
                 pp[blk][r >> 1] = pack_bf16(sc[blk][r - 1], pr);
                 pd[blk][r >> 1] = pack_bf16(dpc[blk][r - 1], ds);
             }
         };
         // Vector work of slot k: L and D of a block are read half a block of
-        // products before its P, dS; then the elements.
+        // products before its P, dS; then the staged elements.
         auto vector_work = [&](int k) {
             const int rl = k - NS / 2;                        // block 0 reads: slots NS/2 .. NS/2+3
             if (rl >= 0 && rl < 4) {
@@ -1067,14 +1069,18 @@ void bwd_kv_kernel(const BwdParams p) {
                 lv[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
                 dd[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + BR + ql);
             }
-            if (k >= NS && k < 2 * NS) {
-                constexpr int E = 16 / NS;
 #pragma unroll
-                for (int i = 0; i < E; ++i) element(0, (k - NS) * E + i);
-            } else if (k >= 2 * NS && k < 2 * NS + NG) {
-                constexpr int E = 16 / NG;
+            for (int blk = 0; blk < 2; ++blk) {
+                const int start = blk ? 2 * NS : NS;          // first slot of the block's elements
+                const int E = 16 / (blk ? NG : NS);           // elements per slot
+                const int t = k - start;
 #pragma unroll
-                for (int i = 0; i < E; ++i) element(1, (k - 2 * NS) * E + i);
+                for (int i = 0; i < E; ++i) {
+                    const int ra = t * E + i, rb = (t - 1) * E + i, rc = (t - 2) * E + i;
+                    if (rc >= 0 && rc < 16) stage_c(blk, rc);
+                    if (rb >= 0 && rb < 16) stage_b(blk, rb);
+                    if (ra >= 0 && ra < 16) stage_a(blk, ra);
+                }
             }
         };
         // Causal mask of block blk, once its scores are complete: only a block
