@@ -16,7 +16,6 @@ Prints ONE JSON line on stdout (progress goes to stderr).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,31 +28,24 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd & bwd (bf16, d=128, causal) and % of MI355X MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_hbm_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_26_amd", "csrc", f)
-                  for f in ("fa2_bwd.hip", "fa2_device.h", "fa2_kernels.h")]   # the dominant kernel's sources
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_kv_kernel_b4_h16_n8192_d128_causal_hbm_traffic.json")
+COPY_PROBE_BYTES = 512 << 20     # plain device copy timed by --probe to calibrate the HBM byte counters
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
 def measured_traffic(launches_per_dispatch: float = 1.0):
-    """HBM bytes per launch of the backward main kernel from committed rocprofv3
-    counter runs, or None when absent or taken on a different kernel source."""
+    """HBM bytes per launch of the backward K/V-tile kernel from committed
+    rocprofv3 counter runs, or None when absent or taken on a different
+    kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from exact_io_aware_26_amd.profiling import kernel_source_digest
     if t.get("source_sha256") != kernel_source_digest():
         return None
     return float(t["bytes_per_launch"]) * launches_per_dispatch
@@ -104,6 +96,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence forward figure")
+    ap.add_argument("--probe", action="store_true",
+                    help="for profilers: one plain copy of known size, then one forward and each backward "
+                         "stage once; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path, so --gpus {args.gpus} "
@@ -142,6 +137,21 @@ def main() -> int:
     def bwd(stages):
         fa2.backward(q, k, v, o, lse, do, causal=w.causal, workspace=ws, grads=grads, stages=stages)
 
+    if args.probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)                     # reads and writes COPY_PROBE_BYTES each
+        torch.cuda.synchronize()
+        del src, dst
+        fwd()
+        for stages in (fa2.BWD_PREPROCESS, fa2.BWD_MAIN, fa2.BWD_FINALIZE):
+            bwd(stages)
+        torch.cuda.synchronize()
+        log("probe done")
+        return 0
+
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         fwd()
@@ -177,14 +187,14 @@ def main() -> int:
     log(f"step {ms_per_step:.3f} ms: fwd {fwd_ms:.3f} ms, bwd D {pre_ms:.3f} + dK/dV loop {main_ms:.3f} "
         f"+ dQ pass {dq_ms:.3f} ms")
 
-    # The dominant kernel is the backward K/V-tile loop (bwd_pair_kernel).  Its
+    # The dominant kernel is the backward K/V-tile loop (bwd_kv_kernel).  Its
     # algorithmic work is 4 of the backward's 5 products (S, dP, dV, dK), i.e.
     # 4/5 of the backward FLOPs; the dQ pass does the fifth (plus its recompute).
     main_flops = 0.8 * bwd_f
     main_tflops = main_flops / (main_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     roofline = {
-        "kernel": "bwd_pair_kernel<128, causal> (backward K/V-tile loop: S, dP, dV, dK)",
+        "kernel": "bwd_kv_kernel<128, causal> (backward K/V-tile loop: S, dP, dV, dK)",
         "bound": "mfma",
         "achieved": main_tflops,
         "peak": PEAK_BF16_TFLOPS,
