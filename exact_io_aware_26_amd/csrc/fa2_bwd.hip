@@ -1043,15 +1043,32 @@ void bwd_kv_kernel(const BwdParams p) {
         // block, this lane's key) in three stages -- c*s - L log2 e, exp2, then
         // dS and the bf16 packing -- run for elements r, r-1, r-2 in one slot,
         // so the instructions of a slot do not wait on each other.
-        auto stage_a = [&](int blk, int r) { sc[blk][r] = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]); };
-        auto stage_b = [&](int blk, int r) { sc[blk][r] = exp2_fast(sc[blk][r]); };
+        // Each stage's result is pinned in its slot (an empty asm that redefines
+        // it), or the compiler sinks the arithmetic down to the dV / dK products
+        // that consume it and the slots before those get no vector work.
+        auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+        auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
+        auto stage_a = [&](int blk, int r) {
+            float x = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]);
+            pin(x);
+            sc[blk][r] = x;
+        };
+        auto stage_b = [&](int blk, int r) {
+            float x = exp2_fast(sc[blk][r]);
+            pin(x);
+            sc[blk][r] = x;
+        };
         auto stage_c = [&](int blk, int r) {
             const float pr = sc[blk][r];
-            const float ds = pr * (dpc[blk][r] - dd[blk][r >> 2][r & 3]);
+            float ds = pr * (dpc[blk][r] - dd[blk][r >> 2][r & 3]);
+            pin(ds);
             dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
             if (r & 1) {
-                pp[blk][r >> 1] = pack_bf16(sc[blk][r - 1], pr);
-                pd[blk][r >> 1] = pack_bf16(dpc[blk][r - 1], ds);
+                uint32_t a = pack_bf16(sc[blk][r - 1], pr), c = pack_bf16(dpc[blk][r - 1], ds);
+                pin_u(a);
+                pin_u(c);
+                pp[blk][r >> 1] = a;
+                pd[blk][r >> 1] = c;
             }
         };
         // Vector work of slot k: L and D of a block are read half a block of
