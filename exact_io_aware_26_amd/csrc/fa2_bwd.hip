@@ -952,29 +952,55 @@ void bwd_kv_kernel(const BwdParams p) {
     const int n_i = n_qt - i_begin;
     const int n_iter = n_i * p.G;
 
-    // Copy query tile `it` into LDS: Q and dO rows (clamped to N-1 past the
-    // end; those rows have L = +inf, so P = dS = 0), and the padded L log2 e
-    // and D rows (waves 0 and 2 both copy L, 1 and 3 both copy D: identical
-    // bytes, so every wave issues the same number of copies).
-    auto copy_tile = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
+    // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
+    // tile program spreads over the slots of its last phase: Q and dO rows
+    // (clamped to N-1 past the end; those rows have L = +inf, so P = dS = 0),
+    // and the padded L log2 e and D rows (waves 0 and 2 both copy L, 1 and 3
+    // both copy D: identical bytes, so every wave issues the same number of
+    // copies).
+    constexpr int NCOPY = 2 * PERW + 1;
+    struct TileCopy {
+        const char* qbase;
+        const char* obase;
+        const float* ld_src;
+        int last, lr, lc;
+        FA2_LDS char* Qd;
+        FA2_LDS char* Od;
+        FA2_LDS float* Ld;
+    };
+    auto plan_copy = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
         const int hq = hk * p.G + it / n_i;
         const int qt0 = (i_begin + it % n_i) * BR;
         const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
-        const char* qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
-        const char* obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
-        const int last = N - 1 - qt0;
-        int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
-        asm volatile("" : "+v"(lr), "+v"(lc));   // rebuilt per tile instead of held across the loop
-#pragma unroll
-        for (int i = 0; i < PERW; ++i) {
-            const int R = (wave * PERW + i) * RPI;
-            const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<RB>(R))));
-            copy_to_lds16(qbase, off, Qd + (wave * PERW + i) * 1024);
-            copy_to_lds16(obase, off, Od + (wave * PERW + i) * 1024);
-        }
         const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
-        const float* src = (wave & 1) ? p.Dsum + prow : p.L2 + prow;
-        copy_to_lds4(src, 4 * lane, Ld + (wave & 1) * BR);
+        TileCopy c;
+        c.qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
+        c.obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
+        c.ld_src = (wave & 1) ? p.Dsum + prow : p.L2 + prow;
+        c.last = N - 1 - qt0;
+        c.lr = lane / CPR;
+        c.lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
+        asm volatile("" : "+v"(c.lr), "+v"(c.lc));   // rebuilt per tile instead of held across the loop
+        c.Qd = Qd;
+        c.Od = Od;
+        c.Ld = Ld;
+        return c;
+    };
+    auto copy_part = [&](const TileCopy& c, int j) {
+        if (j < 2 * PERW) {
+            const int i = j % PERW;
+            const int R = (wave * PERW + i) * RPI;
+            const uint32_t off = (uint32_t)(min(R + c.lr, c.last) * RB + (c.lc ^ (16 * swz<RB>(R))));
+            if (j < PERW) copy_to_lds16(c.qbase, off, c.Qd + (wave * PERW + i) * 1024);
+            else copy_to_lds16(c.obase, off, c.Od + (wave * PERW + i) * 1024);
+        } else {
+            copy_to_lds4(c.ld_src, 4 * lane, c.Ld + (wave & 1) * BR);
+        }
+    };
+    auto copy_tile = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
+        const TileCopy c = plan_copy(it, Qd, Od, Ld);
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) copy_part(c, j);
     };
 
     // LDS operand addresses: the swizzle only flips bits 4.. of a row's byte
@@ -1000,7 +1026,9 @@ void bwd_kv_kernel(const BwdParams p) {
     constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = 2 * NS + 2 * NG;
     constexpr int kPrefetch = 4;
     static_assert(16 % NS == 0 && 16 % NG == 0 && NS >= 8, "slot program shape");
-    auto tile = [&](const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls, int qt0) {
+    static_assert(NCOPY <= NG, "the copies of the next tile fit in the last phase");
+    auto tile = [&](const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls, int qt0,
+                    const TileCopy& cp) {
         int kb = kb_lane, vb1 = vb1_lane, vb2 = vb2_lane;
         asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2));   // rebuilt per tile, not held across the loop
         f32x16 sc[2], dpc[2];
@@ -1117,6 +1145,8 @@ void bwd_kv_kernel(const BwdParams p) {
             if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
             product(k, a);
             vector_work(k);
+            const int jc = k - (2 * NS + NG);               // the next tile's copies: last phase
+            if (jc >= 0 && jc < NCOPY) copy_part(cp, jc);
         };
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
@@ -1135,9 +1165,8 @@ void bwd_kv_kernel(const BwdParams p) {
                     FA2_LDS char* Qw, FA2_LDS char* Ow, FA2_LDS float* Lw) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        copy_tile(min(it + 2, n_iter - 1), Qw, Ow, Lw);
-        tile(Qs, Os, Ls, (i_begin + it % n_i) * BR);
-        wait_vm_keep<2 * PERW + 1>();   // tile it+1, issued one step earlier, has landed
+        tile(Qs, Os, Ls, (i_begin + it % n_i) * BR, plan_copy(min(it + 2, n_iter - 1), Qw, Ow, Lw));
+        wait_vm_keep<NCOPY>();          // tile it+1, issued one step earlier, has landed
         barrier_lds();
     };
 
