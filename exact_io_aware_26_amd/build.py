@@ -23,7 +23,7 @@ SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip"]
 # results straight into vector arithmetic; with this option the compiler keeps
 # those results in ordinary VGPRs instead of accumulation registers that would
 # have to be copied out first.
-SOURCE_FLAGS = {"fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"]}
 
 ARCH = "gfx950"
 FLAGS = [
