@@ -523,19 +523,17 @@ void fwd_pipe_kernel(const FwdParams p) {
         barrier_lds();
     };
 
-    // Unrolled by six: three buffer phases times two score arrays.
+    // Unrolled by six: three buffer phases times two score arrays.  Each step
+    // after the first is guarded on its own rather than leaving the loop with
+    // a break: with six exits the compiler copied the score arrays into fixed
+    // registers at every step instead of alternating them.
     for (int j = 0; j < n_kv; j += 6) {
         step(j, K1, V0, K0, V2, sa, sb);
-        if (j + 1 >= n_kv) break;
-        step(j + 1, K2, V1, K1, V0, sb, sa);
-        if (j + 2 >= n_kv) break;
-        step(j + 2, K0, V2, K2, V1, sa, sb);
-        if (j + 3 >= n_kv) break;
-        step(j + 3, K1, V0, K0, V2, sb, sa);
-        if (j + 4 >= n_kv) break;
-        step(j + 4, K2, V1, K1, V0, sa, sb);
-        if (j + 5 >= n_kv) break;
-        step(j + 5, K0, V2, K2, V1, sb, sa);
+        if (j + 1 < n_kv) step(j + 1, K2, V1, K1, V0, sb, sa);
+        if (j + 2 < n_kv) step(j + 2, K0, V2, K2, V1, sa, sb);
+        if (j + 3 < n_kv) step(j + 3, K1, V0, K0, V2, sb, sa);
+        if (j + 4 < n_kv) step(j + 4, K2, V1, K1, V0, sa, sb);
+        if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
     }
     wait_vm_all();
 
