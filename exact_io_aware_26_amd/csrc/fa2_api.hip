@@ -268,7 +268,7 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
     p.dQ = static_cast<uint16_t*>(dQ);
     p.dK = static_cast<uint16_t*>(dK);
     p.dV = static_cast<uint16_t*>(dV);
-    p.Dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.d_off);
+    p.Dneg = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.d_off);
     p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.l2_off);
     p.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off);
     p.B = B;

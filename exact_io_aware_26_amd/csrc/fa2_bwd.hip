@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
     if (rp < rows_pad && part == 0) {
-        p.Dsum[rp] = acc;
+        p.Dneg[rp] = -acc;
         p.L2[rp] = valid ? p.L[row] * kLog2e : kInf;
     }
 }
@@ -264,7 +264,7 @@ void bwd_main_kernel(const BwdParams p) {
             // so nothing here waits for these loads to land.
             const size_t r = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(qt0 + tid, N - 1);
             sl = p.L2[r];
-            sd = p.Dsum[r];
+            sd = -p.Dneg[r];
         }
     };
 
@@ -556,7 +556,7 @@ void bwd_pair_kernel(const BwdParams p) {
         if (tid < BR) {   // raw values from a clamped row; scaled and masked when stored
             const size_t r = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(qt0 + tid, N - 1);
             sl = p.L2[r];
-            sd = p.Dsum[r];
+            sd = p.Dneg[r];
         }
     };
 
@@ -616,7 +616,7 @@ void bwd_pair_kernel(const BwdParams p) {
         if (tid < BR) {
             const bool in = qt0 + tid < N;
             Ls[tid] = in ? sl : kInf;   // rows past the end get P = 0
-            Dl[tid] = in ? sd : 0.f;
+            Dl[tid] = in ? sd : 0.f;   // -D
         }
         __syncthreads();                         // (A)
 
@@ -626,7 +626,15 @@ void bwd_pair_kernel(const BwdParams p) {
 
         // 3. query block h: S, dP, P, dS for this pair's keys; publish P^T, dS^T.
         {
-            f32x16 s = zero16(), dp = zero16();
+            // dP starts from -D (four consecutive queries per load, in register
+            // order), so the products end at dP - D.
+            f32x16 s = zero16(), dp;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const f32x4 nd = *reinterpret_cast<const FA2_LDS f32x4*>(Dl + 32 * h + 8 * rq + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp[4 * rq + e] = nd[e];
+            }
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const bf16x8 aq = row_operand<RB_D>(Qs, 32 * h, 16 * ks, lane);
@@ -646,13 +654,12 @@ void bwd_pair_kernel(const BwdParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int ql = 32 * h + 8 * rq + 4 * g;          // local query of register 4*rq
                 const f32x4 lv = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
-                const f32x4 dd = *reinterpret_cast<const FA2_LDS f32x4*>(Dl + ql);
                 float pr[4], dsr[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * rq + e;
                     pr[e] = exp2_fast(fmaf(s[r], p.c, -lv[e]));
-                    dsr[e] = pr[e] * (dp[r] - dd[e]);
+                    dsr[e] = pr[e] * dp[r];
                 }
                 const int pos = 32 * h + swap23(8 * rq + 4 * g);   // 4 queries stay contiguous
                 const int off = tile_off<RB_Q>(32 * kvb + li, pos);
@@ -771,7 +778,7 @@ void bwd_dq_kernel(const BwdParams p) {
     }
     const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
     const float l2 = q < N ? p.L2[row] : kInf;   // rows past the end: P = 0
-    const float dq_d = q < N ? p.Dsum[row] : 0.f;
+    const float dq_d = q < N ? -p.Dneg[row] : 0.f;
 
     int n_kv = (N + BC - 1) / BC;
     if (CAUSAL) n_kv = (min(q0 + BRQ, N) - 1) / BC + 1;
@@ -942,7 +949,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     }
     const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
     const float l2 = q < N ? p.L2[row] : kInf;   // rows past the end: P = 0
-    const float dq_d = q < N ? p.Dsum[row] : 0.f;
+    const float neg_d = q < N ? p.Dneg[row] : 0.f;   // -D
 
     // Key blocks (32 keys) and tiles (64 keys) this workgroup walks.
     const int n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
@@ -999,7 +1006,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     // The dp products of a block start from -D, so they end at dp - D.
     f32x16 negd;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
+    for (int r = 0; r < 16; ++r) negd[r] = neg_d;
     f32x16 sc[2], dpc[2];             // s, dp - D of a block, by block parity
     uint32_t dsp[2][8];               // dS^T of a block as packed bf16 B operands, by parity
 #pragma unroll
@@ -1178,18 +1185,16 @@ void bwd_kv_kernel(const BwdParams p) {
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int PERW = kTile / 1024 / NW;   // copy instructions per wave per tensor
     static_assert(BR == 64 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
-    __shared__ __attribute__((aligned(16))) char Qa0[kTile], Qa1[kTile], Qa2[kTile];
-    __shared__ __attribute__((aligned(16))) char Oa0[kTile], Oa1[kTile], Oa2[kTile];
-    __shared__ __attribute__((aligned(16))) float La0[2 * BR], La1[2 * BR], La2[2 * BR];   // [L log2 e | D]
-    FA2_LDS char* const Q0 = (FA2_LDS char*)Qa0;
-    FA2_LDS char* const Q1 = (FA2_LDS char*)Qa1;
-    FA2_LDS char* const Q2 = (FA2_LDS char*)Qa2;
-    FA2_LDS char* const O0 = (FA2_LDS char*)Oa0;
-    FA2_LDS char* const O1 = (FA2_LDS char*)Oa1;
-    FA2_LDS char* const O2 = (FA2_LDS char*)Oa2;
-    FA2_LDS float* const L0 = (FA2_LDS float*)La0;
-    FA2_LDS float* const L1 = (FA2_LDS float*)La1;
-    FA2_LDS float* const L2b = (FA2_LDS float*)La2;
+    // One LDS array per buffered query tile, [Q | dO | L log2 e | -D], each
+    // 256-byte aligned: every read of a tile is a per-tile lane base (with the
+    // array's address folded in) XOR a constant, plus an immediate offset
+    // below 64 KiB.
+    constexpr int kBuf = 2 * kTile + 2 * BR * 4;
+    static_assert(kBuf % 256 == 0, "tile arrays keep the 256-byte alignment the swizzle needs");
+    __shared__ __attribute__((aligned(256))) char Ta0[kBuf], Ta1[kBuf], Ta2[kBuf];
+    FA2_LDS char* const T0 = (FA2_LDS char*)Ta0;
+    FA2_LDS char* const T1 = (FA2_LDS char*)Ta1;
+    FA2_LDS char* const T2 = (FA2_LDS char*)Ta2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1236,8 +1241,8 @@ void bwd_kv_kernel(const BwdParams p) {
     // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
     // tile program spreads over the slots of its last phase: Q and dO rows
     // (clamped to N-1 past the end; those rows have L = +inf, so P = dS = 0),
-    // and the padded L log2 e and D rows (waves 0 and 2 both copy L, 1 and 3
-    // both copy D: identical bytes, so every wave issues the same number of
+    // and the padded L log2 e and -D rows (waves 0 and 2 both copy L, 1 and 3
+    // both copy -D: identical bytes, so every wave issues the same number of
     // copies).
     constexpr int NCOPY = 2 * PERW + 1;
     struct TileCopy {
@@ -1245,11 +1250,9 @@ void bwd_kv_kernel(const BwdParams p) {
         const char* obase;
         const float* ld_src;
         int last, lr, lc;
-        FA2_LDS char* Qd;
-        FA2_LDS char* Od;
-        FA2_LDS float* Ld;
+        FA2_LDS char* T;
     };
-    auto plan_copy = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
+    auto plan_copy = [&](int it, FA2_LDS char* T) {
         const int hq = hk * p.G + it / n_i;
         const int qt0 = (i_begin + it % n_i) * BR;
         const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
@@ -1257,14 +1260,12 @@ void bwd_kv_kernel(const BwdParams p) {
         TileCopy c;
         c.qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
         c.obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
-        c.ld_src = (wave & 1) ? p.Dsum + prow : p.L2 + prow;
+        c.ld_src = (wave & 1) ? p.Dneg + prow : p.L2 + prow;
         c.last = N - 1 - qt0;
         c.lr = lane / CPR;
         c.lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
         asm volatile("" : "+v"(c.lr), "+v"(c.lc));   // rebuilt per tile instead of held across the loop
-        c.Qd = Qd;
-        c.Od = Od;
-        c.Ld = Ld;
+        c.T = T;
         return c;
     };
     auto copy_part = [&](const TileCopy& c, int j) {
@@ -1272,14 +1273,14 @@ void bwd_kv_kernel(const BwdParams p) {
             const int i = j % PERW;
             const int R = (wave * PERW + i) * RPI;
             const uint32_t off = (uint32_t)(min(R + c.lr, c.last) * RB + (c.lc ^ (16 * swz<RB>(R))));
-            if (j < PERW) copy_to_lds16(c.qbase, off, c.Qd + (wave * PERW + i) * 1024);
-            else copy_to_lds16(c.obase, off, c.Od + (wave * PERW + i) * 1024);
+            if (j < PERW) copy_to_lds16(c.qbase, off, c.T + (wave * PERW + i) * 1024);
+            else copy_to_lds16(c.obase, off, c.T + kTile + (wave * PERW + i) * 1024);
         } else {
-            copy_to_lds4(c.ld_src, 4 * lane, c.Ld + (wave & 1) * BR);
+            copy_to_lds4(c.ld_src, 4 * lane, c.T + 2 * kTile + (wave & 1) * BR * 4);
         }
     };
-    auto copy_tile = [&](int it, FA2_LDS char* Qd, FA2_LDS char* Od, FA2_LDS float* Ld) {
-        const TileCopy c = plan_copy(it, Qd, Od, Ld);
+    auto copy_tile = [&](int it, FA2_LDS char* T) {
+        const TileCopy c = plan_copy(it, T);
 #pragma unroll
         for (int j = 0; j < NCOPY; ++j) copy_part(c, j);
     };
@@ -1308,35 +1309,44 @@ void bwd_kv_kernel(const BwdParams p) {
     constexpr int kPrefetch = 4;
     static_assert(16 % NS == 0 && 16 % NG == 0 && NS >= 8, "slot program shape");
     static_assert(NCOPY <= NG, "the copies of the next tile fit in the last phase");
-    auto tile = [&](const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls, int qt0,
-                    const TileCopy& cp) {
-        int kb = kb_lane, vb1 = vb1_lane, vb2 = vb2_lane;
-        asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2));   // rebuilt per tile, not held across the loop
+    auto tile = [&](const FA2_LDS char* T, int qt0, const TileCopy& cp) {
+        // Lane bases with the tile's address folded in, rebuilt per tile (opaque
+        // to the compiler) rather than held across the loop.
+        const uint32_t tb = (uint32_t)(uintptr_t)T;
+        uint32_t kb = tb + kb_lane, vb1 = tb + vb1_lane, vb2 = tb + vb2_lane, lb = tb + 2 * kTile + 16 * g;
+        asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2), "+v"(lb));
+        auto at = [](uint32_t a) { return (const FA2_LDS char*)(uintptr_t)a; };
+        // Four consecutive floats of the L log2 e (which = 0) or -D (which = 1)
+        // rows: queries 32 * blk + 8 * rl + 4g .. +3, the order of a score
+        // accumulator's registers 4 rl .. 4 rl + 3.
+        auto ld_rows = [&](int which, int blk, int rl) {
+            return *reinterpret_cast<const FA2_LDS f32x4*>(at(lb) + 4 * (which * BR + 32 * blk + 8 * rl));
+        };
         f32x16 sc[2], dpc[2];
         uint32_t pp[2][8], pd[2][8];
-        f32x4 lv[2][4], dd[2][4];
+        f32x4 lv[2][4];
+        f32x16 nd[2];                        // -D of each block: where its dP products start
+        auto load_nd = [&](int blk, int rl) {
+            const f32x4 v = ld_rows(1, blk, rl);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            sc[i] = zero16();
-            dpc[i] = zero16();
-        }
+            for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
+        };
         // A operand of product k.
         auto load_a = [&](int k) -> bf16x8 {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
-                const FA2_LDS char* t = (k & 1) ? Os : Qs;
-                return as_bf16x8(lds_load16(t + 32 * blk * RB + (kb ^ (32 * ks))));
+                const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
+                return as_bf16x8(lds_load16(at(kb ^ (32 * ks)) + off));
             }
             const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
-            const FA2_LDS char* t = (jj & 1) ? Qs : Os;
-            const int base = 16 * (2 * blk + h) * RB;
-            return cat_tr(lds_load_tr(t + base + (vb1 ^ (64 * db))), lds_load_tr(t + base + (vb2 ^ (64 * db))));
+            const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
+            return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
         };
         auto product = [&](int k, bf16x8 a) {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
-                if (k & 1) dpc[blk] = mfma32(a, vf[ks], dpc[blk]);
-                else sc[blk] = mfma32(a, kf[ks], sc[blk]);
+                if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
+                else sc[blk] = mfma32(a, kf[ks], ks == 0 ? zero16() : sc[blk]);
                 return;
             }
             const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
@@ -1369,7 +1379,7 @@ void bwd_kv_kernel(const BwdParams p) {
         };
         auto stage_c = [&](int blk, int r) {
             const float pr = sc[blk][r];
-            float ds = pr * (dpc[blk][r] - dd[blk][r >> 2][r & 3]);
+            float ds = pr * dpc[blk][r];
             pin(ds);
             dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
             if (r & 1) {
@@ -1380,21 +1390,16 @@ void bwd_kv_kernel(const BwdParams p) {
                 pd[blk][r >> 1] = c;
             }
         };
-        // Vector work of slot k: L and D of a block are read half a block of
-        // products before its P, dS; then the staged elements.
+        // Vector work of slot k: L of a block is read half a block of products
+        // before its P, -D of block 1 with L of block 0; then the staged elements.
         auto vector_work = [&](int k) {
-            const int rl = k - NS / 2;                        // block 0 reads: slots NS/2 .. NS/2+3
+            const int rl = k - NS / 2;                        // slots NS/2 .. NS/2+3
             if (rl >= 0 && rl < 4) {
-                const int ql = 8 * rl + 4 * g;
-                lv[0][rl] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
-                dd[0][rl] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + BR + ql);
+                lv[0][rl] = ld_rows(0, 0, rl);
+                load_nd(1, rl);
             }
-            const int rl1 = k - (NS + NS / 2);                // block 1 reads
-            if (rl1 >= 0 && rl1 < 4) {
-                const int ql = 32 + 8 * rl1 + 4 * g;
-                lv[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + ql);
-                dd[1][rl1] = *reinterpret_cast<const FA2_LDS f32x4*>(Ls + BR + ql);
-            }
+            const int rl1 = k - (NS + NS / 2);                // block 1's L
+            if (rl1 >= 0 && rl1 < 4) lv[1][rl1] = ld_rows(0, 1, rl1);
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 const int start = blk ? 2 * NS : NS;          // first slot of the block's elements
@@ -1419,6 +1424,9 @@ void bwd_kv_kernel(const BwdParams p) {
                     if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk][i] = -kInf;
             }
         };
+        // -D of block 0 before the first operands: its dP products start at slot 1.
+#pragma unroll
+        for (int rl = 0; rl < 4; ++rl) load_nd(0, rl);
         bf16x8 abuf[kPrefetch];
         auto slot = [&](int k) {
             __builtin_amdgcn_sched_barrier(0);
@@ -1442,25 +1450,24 @@ void bwd_kv_kernel(const BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto step = [&](int it, const FA2_LDS char* Qs, const FA2_LDS char* Os, const FA2_LDS float* Ls,
-                    FA2_LDS char* Qw, FA2_LDS char* Ow, FA2_LDS float* Lw) __attribute__((always_inline)) {
+    auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        tile(Qs, Os, Ls, (i_begin + it % n_i) * BR, plan_copy(min(it + 2, n_iter - 1), Qw, Ow, Lw));
+        tile(T, (i_begin + it % n_i) * BR, plan_copy(min(it + 2, n_iter - 1), Tw));
         wait_vm_keep<NCOPY>();          // tile it+1, issued one step earlier, has landed
         barrier_lds();
     };
 
     if (n_iter > 0) {
-        copy_tile(0, Q0, O0, L0);
-        if (n_iter > 1) copy_tile(1, Q1, O1, L1);
+        copy_tile(0, T0);
+        if (n_iter > 1) copy_tile(1, T1);
         wait_vm_all();
         __syncthreads();
         for (int it = 0; it < n_iter; it += 3) {
-            step(it, Q0, O0, L0, Q2, O2, L2b);
+            step(it, T0, T2);
             if (it + 1 < n_iter) {
-                step(it + 1, Q1, O1, L1, Q0, O0, L0);
-                if (it + 2 < n_iter) step(it + 2, Q2, O2, L2b, Q1, O1, L1);
+                step(it + 1, T1, T0);
+                if (it + 2 < n_iter) step(it + 2, T2, T1);
             }
         }
         wait_vm_all();

@@ -26,7 +26,7 @@ struct BwdParams {
     uint16_t* dQ;
     uint16_t* dK;
     uint16_t* dV;
-    float* Dsum;   // fp32 [B, Hq, Npad]  workspace: D = rowsum(dO o O); 0 past N
+    float* Dneg;   // fp32 [B, Hq, Npad]  workspace: -D = -rowsum(dO o O); 0 past N
     float* L2;     // fp32 [B, Hq, Npad]  workspace: L * log2(e); +inf past N (P = 0 there)
     float* dQacc;  // fp32 [B, Hq, N, D]  workspace: dQ accumulated with atomics
     int B, Hq, Hkv, N, G;

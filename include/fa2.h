@@ -85,7 +85,7 @@ fa2_status fa2_fwd(const void *Q, const void *K, const void *V, void *O, float *
 
 /*
  * Bytes of device workspace fa2_bwd needs: two fp32 [B,Hq,Npad] arrays
- * (Npad = N rounded up to a multiple of 64) holding D = rowsum(dO o O) and
+ * (Npad = N rounded up to a multiple of 64) holding -D = -rowsum(dO o O) and
  * L * log2(e) per query row, and an fp32 [B,Hq,N,d] array accumulating dQ in
  * the atomic mode, each starting on a 256-byte boundary.  Returns 0 for an
  * empty problem and for sizes fa2_bwd rejects (negative, Hq % Hkv != 0,
