@@ -370,17 +370,31 @@ void fwd_pipe_kernel(const FwdParams p) {
     // so it fetches the chunk the swizzle puts in that slot.  R is a multiple
     // of RPI, and for these row strides swz(R + r) = swz(r) ^ swz(R) for
     // r < RPI.  Rows past the end repeat row N-1 (their keys are masked).
+    // Byte offsets of this lane's chunks in a whole tile (held for the loop);
+    // only the tile that ends past N recomputes them, clamped.
+    uint32_t off_full[PERW];
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+        const int R = (wave * PERW + i) * RPI;
+        const int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
+        off_full[i] = (uint32_t)((R + lr) * RB + (lc ^ (16 * swz<D>(R))));
+    }
     auto copy_tile = [&](const uint16_t* head, int t, FA2_LDS char* dst) {
         const int kv0 = t * BC;
         const char* base = reinterpret_cast<const char*>(head + (size_t)kv0 * D);
         const int last = N - 1 - kv0;
-        int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
-        asm volatile("" : "+v"(lr), "+v"(lc));   // rebuilt per tile instead of held across the loop
+        if (last >= BC - 1) {
 #pragma unroll
-        for (int i = 0; i < PERW; ++i) {
-            const int R = (wave * PERW + i) * RPI;
-            const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<D>(R))));
-            copy_to_lds16(base, off, dst + (wave * PERW + i) * 1024);
+            for (int i = 0; i < PERW; ++i) copy_to_lds16(base, off_full[i], dst + (wave * PERW + i) * 1024);
+        } else {
+            int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
+            asm volatile("" : "+v"(lr), "+v"(lc));
+#pragma unroll
+            for (int i = 0; i < PERW; ++i) {
+                const int R = (wave * PERW + i) * RPI;
+                const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<D>(R))));
+                copy_to_lds16(base, off, dst + (wave * PERW + i) * 1024);
+            }
         }
     };
 
@@ -502,6 +516,10 @@ void fwd_pipe_kernel(const FwdParams p) {
         if (j < n_w) {
             mask(j, s_cur);
             uint32_t pp[2][8];
+            // Raised priority while this wave interleaves S_{j+1} with the
+            // softmax of S_j, normal for the P V products: the other wave on the
+            // SIMD then fills the matrix unit's idle slots of the mixed phase.
+            __builtin_amdgcn_s_setprio(1);
             scores(Ks, s_next);
             const float alpha = softmax(s_cur, pp);
             // Materialize P here, beside the S_{j+1} products, rather than
@@ -516,6 +534,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
             }
+            __builtin_amdgcn_s_setprio(0);
             pv(Vs, pp);
             row_sum(s_cur, alpha);
         }
