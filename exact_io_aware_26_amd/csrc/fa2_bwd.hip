@@ -13,12 +13,21 @@
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
 //     dK = scale * dS^T Q,  dQ = scale * dS K.
 //
-// Three kernels on one stream:
-//   bwd_pre        D = rowsum(dO o O) in fp32, and zeroes the fp32 dQ accumulator.
-//   bwd_main       per K/V tile: dK, dV in VGPRs for the whole loop; dQ by atomics.
-//   bwd_dq_convert dQ = bf16(scale * accumulator).
+// Kernels, launched on one stream by fa2_bwd:
+//   bwd_pre          -D = -rowsum(dO o O) and L log2(e) per padded row (fp32);
+//                    in the atomic mode it also zeroes the fp32 dQ accumulator.
+//   bwd_kv           d = 64, 128: one workgroup per 128 keys; dK and dV stay in
+//                    registers over all query tiles (and all query heads of a
+//                    GQA group).
+//   bwd_dq_pipe      d = 64, 128: one workgroup per 128 query rows; dQ stays in
+//                    registers over all key blocks, recomputing S and dP, so no
+//                    atomics are needed and dQ is deterministic.
+//   bwd_main         d = 256: the K/V loop with register-staged tiles; with
+//   bwd_dq           atomic dQ or followed by bwd_dq (the d = 256 dQ pass).
+//   bwd_pair         the pages' atomic accumulation of dQ for d = 64, 128
+//   bwd_dq_convert   (FA2_BWD_DQ_ATOMIC), then dQ = bf16(scale * accumulator).
 //
-// gfx950 mapping of bwd_main (NW wave64s; each wave owns 32 keys of the tile,
+// gfx950 mapping shared by the K/V loops (each wave owns 32 keys of the tile,
 // the backward analogue of splitting Q across waves):
 //   * S = Q K_w^T and dP = dO V_w^T on v_mfma_f32_32x32x16_bf16 with the
 //     wave's K_w / V_w rows as the B operand: every accumulator register then
@@ -27,11 +36,10 @@
 //   * dV^T += dO^T P and dK^T += Q^T dS take P and dS straight from registers
 //     (as bf16) and read dO^T / Q^T fragments with ds_read_b64_tr_b16 from
 //     row-major LDS tiles.
-//   * dQ needs dS with the queries across lanes, so each wave writes its dS^T
-//     block to LDS; after one barrier the waves split the dQ tile, each
-//     reducing over all keys of the workgroup (dS and K both by transposed
-//     LDS reads) and adding its fp32 result into the accumulator with
-//     global atomics (one per element per K/V tile).
+//   * In the atomic mode dQ needs dS with the queries across lanes, so each
+//     wave writes its dS^T block to LDS; after one barrier the waves split the
+//     dQ tile and add their fp32 results into the accumulator with global
+//     atomics (one per element per K/V tile).
 //   * LDS tiles use one XOR swizzle of the 16-byte chunks that is free of
 //     bank conflicts both for 16-byte row reads (MFMA operands) and for the
 //     transposed reads.
@@ -85,11 +93,10 @@ __device__ __forceinline__ bf16x8 row_operand(const FA2_LDS char* tile, int r0, 
     return as_bf16x8(lds_load16(tile + tile_off<RB>(row, col)));
 }
 
-// BC keys per workgroup (32 per wave), BR query rows per inner tile; K_w/V_w
-// MFMA operands live in VGPRs (KV_REGS) or are re-read from LDS.
+// bwd_main (d = 256 only): BC keys per workgroup (32 per wave), BR query rows
+// per inner tile; K_w/V_w MFMA operands live in VGPRs (KV_REGS) or are re-read
+// from LDS.
 template <int D> struct BwdCfg;
-template <> struct BwdCfg<64> { static constexpr int BC = 128, NW = 4, BR = 64; static constexpr bool KV_REGS = true; };
-template <> struct BwdCfg<128> { static constexpr int BC = 128, NW = 4, BR = 64; static constexpr bool KV_REGS = true; };
 template <> struct BwdCfg<256> { static constexpr int BC = 64, NW = 2, BR = 32; static constexpr bool KV_REGS = false; };
 
 // ---------------------------------------------------------------------------------------------
@@ -146,7 +153,6 @@ void bwd_main_kernel(const BwdParams p) {
     constexpr int KSD = D / 16;        // reduction steps over the head dim
     constexpr int NBD = D / 32;        // 32-wide head-dim blocks
     constexpr int NQB = BR / 32;       // 32-row query blocks per tile
-    constexpr int KSQ = BR / 16;       // reduction steps over the queries of a tile
     constexpr int KSKV = BC / 16;      // reduction steps over the keys of the workgroup
     constexpr int kKBytes = BC * RB_D;
     constexpr int kVBytes = KV_REGS ? 0 : BC * RB_D;
@@ -463,7 +469,7 @@ __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1)
 template <int D, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_pair_kernel(const BwdParams p) {
-    constexpr int BC = 128, NW = 8, NT = 512, BR = 64;
+    constexpr int BC = 128, NT = 512, BR = 64;
     constexpr int RB_D = 2 * D;        // bytes per row of K / Q / dO tiles
     constexpr int RB_Q = 2 * BR;       // bytes per row of the P^T / dS^T tiles
     constexpr int KSD = D / 16;        // reduction steps over the head dim (S, dP)

@@ -44,9 +44,7 @@ namespace fa2 {
 
 namespace {
 
-template <int D> struct FwdTile;
-template <> struct FwdTile<64> { static constexpr int BC = 64; };
-template <> struct FwdTile<128> { static constexpr int BC = 64; };
+template <int D> struct FwdTile;   // fwd_kernel (d = 256 only)
 template <> struct FwdTile<256> { static constexpr int BC = 32; };
 
 constexpr int kThreads = 256;

@@ -34,12 +34,20 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_26_amd", "csrc", f)
 COPY_KERNEL = "copyBuffer"     # the runtime's device-to-device copy (torch's copy_ of a uint8 tensor)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
-    """sha256 of the sources of the backward kernels (what the traffic record was taken on)."""
+    """sha256 of the code (comments and layout ignored) of the backward kernels'
+    sources: what the traffic record was taken on."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -56,3 +56,11 @@ def test_trace_averages_the_timed_launches(tmp_path):
     row = [l for l in md.splitlines() if l.startswith("| bwd_kv_kernel")][0]
     assert row.rstrip(" |").endswith("2.0")      # mean of the last two launches, in us
     assert "the command" in md and "2.0 us per launch" in md
+
+
+def test_source_digest_ignores_comments_and_layout():
+    a = "int f(int x) {  // one\n    return x + 1; /* two\n three */ }\n"
+    b = "int f(int x) { return x + 1; }"
+    c = "int f(int x) { return x + 2; }"
+    assert profiling._code_only(a) == profiling._code_only(b)
+    assert profiling._code_only(b) != profiling._code_only(c)
