@@ -19,7 +19,7 @@
 //   bwd_kv           d = 64, 128: one workgroup per 128 keys; dK and dV stay in
 //                    registers over all query tiles (and all query heads of a
 //                    GQA group).
-//   bwd_dq_pipe      d = 64, 128: one workgroup per 128 query rows; dQ stays in
+//   bwd_dq_pipe      d = 64, 128: one workgroup per 256 query rows; dQ stays in
 //                    registers over all key blocks, recomputing S and dP, so no
 //                    atomics are needed and dQ is deterministic.
 //   bwd_main         d = 256: the K/V loop with register-staged tiles; with
@@ -885,36 +885,41 @@ void bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // bwd_dq_pipe: the dQ pass for d = 64 and 128.
 //
-// One workgroup = 4 wave64s = 128 query rows, one wave per SIMD.  Each wave
-// keeps its 32 rows of Q and dO as MFMA B operands and its dQ^T accumulator in
-// registers, all transposed so that each lane owns one query row:
+// One workgroup = 4 wave64s, one wave per SIMD; each wave owns two 32-row query
+// blocks (u = 0, 1; 256 rows per workgroup).  Q and dO of its rows are MFMA B
+// operands in registers and its dQ^T accumulators stay in registers, all
+// transposed so that each lane owns one query row of each block:
 //     s  = K Q^T,  dp = V dO^T          (A: K / V rows from LDS)
 //     P  = exp2(c s - L log2 e),  dS = P o (dp - D)   (masked on the diagonal)
 //     dQ^T += K^T dS^T                  (A: K^T by transposed reads, B: dS^T registers)
-// The keys the causal mask lets through are walked in 32-key blocks; 64-key
-// tiles of K and V are copied into LDS four deep.  Stage s is a fixed program
-// of products, one per slot: the s, dp products of block s alternate (two to
-// one) with the dQ products of block s-2, while the dS of block s-1 is formed
-// element by element over the stage's slots.  So the vector work of a block
-// runs beside the products of its neighbours.  A tile is read in four
+// Every A operand read from LDS feeds the products of both query blocks, and
+// each K / V tile copied into LDS serves 256 query rows.  The keys the causal
+// mask lets through are walked in 32-key blocks; 64-key tiles of K and V are
+// copied into LDS four deep.  Stage s is a fixed program of operand loads,
+// each followed by its two products: the s, dp loads of block s alternate
+// (two to one) with the dQ loads of block s-2, while the dS of block s-1 is
+// formed element by element over the stage's slots, so the vector work of a
+// block runs beside the products of its neighbours.  A tile is read in four
 // consecutive stages; one barrier per tile.  The first two stages read a
 // zeroed "tile -1" and add nothing, and two stages more than there are blocks
 // drain the pipeline.  The stage loop is unrolled by eight so that every
-// buffer offset is a compile-time immediate.
+// buffer offset is a compile-time immediate.  The dQ^T accumulators (128
+// registers at d = 128) live in AGPRs.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_pipe_kernel(const BwdParams p) {
-    constexpr int NW = 4, BRQ = 32 * NW, BT = 64;    // query rows per workgroup, keys per tile
-    constexpr int RB = 2 * D;                         // bytes per K / V tile row
+    constexpr int NW = 4, U = 2, BRQ = 32 * U * NW, BT = 64;
+    constexpr int RB = 2 * D;
     constexpr int kTile = BT * RB;
     constexpr int KSD = D / 16, NBD = D / 32;
-    constexpr int NSD = 2 * KSD;                      // s, dp products per 32-key block
-    constexpr int NQ = 2 * NBD;                       // dQ products per block (two 16-key halves)
-    constexpr int SL = NSD + NQ;                      // slots per stage
+    constexpr int NSD = 2 * KSD;                      // s, dp operand loads per block
+    constexpr int NQ = 2 * NBD;                       // dQ operand loads per block
+    constexpr int SL = NSD + NQ;                      // operand loads (pairs of products) per stage
     constexpr int RPI = 1024 / RB, CPR = RB / 16;
-    constexpr int PERW = kTile / 1024 / NW;           // copy instructions per wave per tensor
+    constexpr int PERW = kTile / 1024 / NW;
     constexpr int NCOPY = 2 * PERW;
     constexpr int kPrefetch = 4;
+    constexpr int NE = 16 * U;                        // dS elements per lane per block
     static_assert(NSD == 2 * NQ && PERW >= 1 && NCOPY <= SL, "stage program shape");
     __shared__ __attribute__((aligned(256))) char Ka[4 * kTile], Va[4 * kTile];
     FA2_LDS char* const Kbuf = (FA2_LDS char*)Ka;
@@ -926,7 +931,6 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     const int g = lane >> 5;
     const int li = lane & 31;
 
-    // Heaviest causal query tiles first; heads of one level on consecutive ids.
     const int n_qtiles = (p.N + BRQ - 1) / BRQ;
     const int BH = p.B * p.Hq;
     const int level = blockIdx.x / BH;
@@ -939,32 +943,33 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
     const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
     const int q0 = qtile * BRQ;
-    const int wq0 = q0 + 32 * wave;
-    const int q = wq0 + li;
+    const int wq0 = q0 + 32 * U * wave;
 
-    bf16x8 qf[KSD], of[KSD];
+    bf16x8 qf[U][KSD], of[U][KSD];
+    float l2[U], dq_d[U];
+    int qu[U];
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-        if (q < N) {
-            a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
-            c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
+    for (int u = 0; u < U; ++u) {
+        const int q = wq0 + 32 * u + li;
+        qu[u] = q;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+            if (q < N) {
+                a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
+                c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
+            }
+            qf[u][ks] = as_bf16x8(a);
+            of[u][ks] = as_bf16x8(c);
         }
-        qf[ks] = as_bf16x8(a);
-        of[ks] = as_bf16x8(c);
+        const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
+        l2[u] = q < N ? p.L2[row] : kInf;
+        dq_d[u] = q < N ? -p.Dneg[row] : 0.f;
     }
-    const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
-    const float l2 = q < N ? p.L2[row] : kInf;   // rows past the end: P = 0
-    const float neg_d = q < N ? p.Dneg[row] : 0.f;   // -D
 
-    // Key blocks (32 keys) and tiles (64 keys) this workgroup walks.
     const int n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
     const int n_t = (n_kb + 1) / 2;
 
-    // Copy of key tile t into buffer `buf` (clamped to the last tile; rows past
-    // the end repeat row N-1 and their keys are masked).  Lane i of a copy
-    // writes bytes 16*i of its 1 KiB, so it fetches the chunk the swizzle puts
-    // there; for these row strides swz(R + r) = swz(r) ^ swz(R) for r < RPI.
     auto copy_part = [&](int t, int buf, int j) {
         const int kv0 = min(t, n_t - 1) * BT;
         const int last = N - 1 - kv0;
@@ -977,18 +982,12 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         copy_to_lds16(src, off, (j < PERW ? Kbuf : Vbuf) + buf * kTile + (wave * PERW + i) * 1024);
     };
 
-    // Operand addresses: the swizzle only flips address bits below the row
-    // stride, so they are a per-lane base XOR a constant (32*ks for K / V
-    // rows; 64*db for transposed reads), plus a buffer offset.
     const int j16 = lane & 15;
     const int xq = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
     const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
     const int kb_lane = li * RB + 16 * (g ^ swz<RB>(li));
     const int vb1_lane = r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1));
     const int vb2_lane = r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2));
-    // One opaque pointer per head-dim step and tensor, so that every read
-    // carries its buffer offset in the instruction's immediate field (the V
-    // array lies past its 64 KiB reach from the K array).
     const FA2_LDS char* kp[KSD];
     const FA2_LDS char* vp[KSD];
     const FA2_LDS char* tp1[NBD];
@@ -1006,123 +1005,132 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         asm volatile("" : "+v"(tp1[db]), "+v"(tp2[db]));
     }
 
-    f32x16 acc[NBD];
+    f32x16 acc[U][NBD];
 #pragma unroll
-    for (int i = 0; i < NBD; ++i) acc[i] = zero16();
-    // The dp products of a block start from -D, so they end at dp - D.
-    f32x16 negd;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) negd[r] = neg_d;
-    f32x16 sc[2], dpc[2];             // s, dp - D of a block, by block parity
-    uint32_t dsp[2][8];               // dS^T of a block as packed bf16 B operands, by parity
+        for (int i = 0; i < NBD; ++i) acc[u][i] = zero16();
+    f32x16 sc[2][U], dpc[2][U];
+    uint32_t dsp[2][U][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        sc[i] = zero16();
-        dpc[i] = zero16();
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) dsp[i][r] = 0u;
-    }
-    // Block -1 (parity 1) gets its dS in the first stage: scores of -inf give
-    // P = 0 (zero scores would give exp2(-L log2 e), which can overflow).
+        for (int u = 0; u < U; ++u) {
+            sc[i][u] = zero16();
+            dpc[i][u] = zero16();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[1][r] = -kInf;
+            for (int r = 0; r < 8; ++r) dsp[i][u][r] = 0u;
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[1][u][r] = -kInf;
 
-    // Stage s (S8 = s mod 8 fixes every buffer): s, dp of block s, dQ of block
-    // s-2, dS of block s-1.  Block x lives in tile x >> 1, buffer (x >> 1) & 3,
-    // rows 32 * (x & 1).
     auto stage = [&](auto s8_tag, int s) __attribute__((always_inline)) {
         constexpr int S8 = decltype(s8_tag)::value;
-        constexpr int P_SD = S8 & 1;                              // parity of block s
-        constexpr int P_EL = P_SD ^ 1;                            // parity of block s-1
-        constexpr int BUF_SD = (S8 >> 1) & 3;                     // buffer of tile s >> 1
-        constexpr int BUF_Q = ((S8 >> 1) + 3) & 3;                // buffer of tile (s - 2) >> 1
+        constexpr int P_SD = S8 & 1;
+        constexpr int P_EL = P_SD ^ 1;
+        constexpr int BUF_SD = (S8 >> 1) & 3;
+        constexpr int BUF_Q = ((S8 >> 1) + 3) & 3;
         constexpr int OFF_SD = BUF_SD * kTile + 32 * P_SD * RB;
-        constexpr int OFF_Q = BUF_Q * kTile + 32 * P_SD * RB;     // block s-2 has the parity of s
+        constexpr int OFF_Q = BUF_Q * kTile + 32 * P_SD * RB;
+
         auto load_a = [&](int k) -> bf16x8 {
-            if (k % 3 != 2) {                                     // s, dp product j
+            if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
                 return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + OFF_SD));
             }
-            const int qq = k / 3, h = qq / NBD, db = qq % NBD;    // dQ product: 16-key half h, d block db
+            const int qq = k / 3, h = qq / NBD, db = qq % NBD;
             const int off = OFF_Q + 16 * h * RB;
             return cat_tr(lds_load_tr(tp1[db] + off), lds_load_tr(tp2[db] + off));
         };
-        auto product = [&](int k, bf16x8 a) {
+        auto product = [&](int k, int u, bf16x8 a) {
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
-                if (j & 1) dpc[P_SD] = mfma32(a, of[ks], ks == 0 ? negd : dpc[P_SD]);   // dp - D
-                else sc[P_SD] = mfma32(a, qf[ks], ks == 0 ? zero16() : sc[P_SD]);
+                if (j & 1) dpc[P_SD][u] = mfma32(a, of[u][ks], ks == 0 ? zero16() : dpc[P_SD][u]);
+                else sc[P_SD][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : sc[P_SD][u]);
                 return;
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
-            const bf16x8 bds = as_bf16x8(u32x4{dsp[P_SD][4 * h], dsp[P_SD][4 * h + 1], dsp[P_SD][4 * h + 2], dsp[P_SD][4 * h + 3]});
-            acc[db] = mfma32(a, bds, acc[db]);
+            const bf16x8 bds = as_bf16x8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
+                                               dsp[P_SD][u][4 * h + 2], dsp[P_SD][u][4 * h + 3]});
+            // Issued as assembly to keep the accumulator in AGPRs (the compiler
+            // places every builtin product's result in VGPRs here, which would
+            // not fit); acc[u][db] is next touched a dozen products later.
+            f32x16 c = acc[u][db];
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
+            acc[u][db] = c;
         };
-
-        // dS of block s-1, element r (key 8*(r/4) + 4g + r%4 of the block, this
-        // lane's query) in three pinned stages, starting at slot r*(SL-3)/15.
         auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
         auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
-        auto el_a = [&](int r) {
-            float x = fmaf(sc[P_EL][r], p.c, -l2);
+        auto el_a = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = fmaf(sc[P_EL][u][r], p.c, -l2[u]);
             pin(x);
-            sc[P_EL][r] = x;
+            sc[P_EL][u][r] = x;
         };
-        auto el_b = [&](int r) {
-            float x = exp2_fast(sc[P_EL][r]);
+        auto el_b = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = exp2_fast(sc[P_EL][u][r]);
             pin(x);
-            sc[P_EL][r] = x;
+            sc[P_EL][u][r] = x;
         };
-        auto el_c = [&](int r) {
-            float x = sc[P_EL][r] * dpc[P_EL][r];
+        auto el_c = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = sc[P_EL][u][r] * (dpc[P_EL][u][r] - dq_d[u]);
             pin(x);
-            dpc[P_EL][r] = x;
+            dpc[P_EL][u][r] = x;
             if (r & 1) {
-                uint32_t u = pack_bf16(dpc[P_EL][r - 1], x);
-                pin_u(u);
-                dsp[P_EL][r >> 1] = u;
+                uint32_t w = pack_bf16(dpc[P_EL][u][r - 1], x);
+                pin_u(w);
+                dsp[P_EL][u][r >> 1] = w;
             }
         };
-        // Mask of block s-1 before its dS: keys above the diagonal or past N.
         {
             const int kb0 = 32 * (s - 1);
             if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if ((CAUSAL && key > q) || key >= N) sc[P_EL][i] = -kInf;
-                }
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                        if ((CAUSAL && key > qu[u]) || key >= N) sc[P_EL][u][i] = -kInf;
+                    }
             }
         }
-        const bool copy_stage = (S8 & 1) == 0;                    // even stages copy tile (s >> 1) + 2
+        const bool copy_stage = (S8 & 1) == 0;
         constexpr int BUF_W = ((S8 >> 1) + 2) & 3;
         const int tcopy = (s >> 1) + 2;
         bf16x8 abuf[kPrefetch];
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+        // 2 * SL product slots: load k feeds slots 2k (u = 0) and 2k + 1 (u = 1).
 #pragma unroll
         for (int k = 0; k < SL; ++k) {
-            __builtin_amdgcn_sched_barrier(0);
             const bf16x8 a = abuf[k % kPrefetch];
-            if (k + kPrefetch < SL) abuf[k % kPrefetch] = load_a(k + kPrefetch);
-            product(k, a);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int sa = r * (SL - 3) / 15;
-                if (k == sa + 2) el_c(r);
-                if (k == sa + 1) el_b(r);
-                if (k == sa) el_a(r);
+            for (int u = 0; u < U; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int slot = U * k + u;
+                if (u == 0 && k + kPrefetch < SL) abuf[k % kPrefetch] = load_a(k + kPrefetch);
+                product(k, u, a);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    const int sa = e * (U * SL - 3) / (NE - 1);
+                    if (slot == sa + 2) el_c(e);
+                    if (slot == sa + 1) el_b(e);
+                    if (slot == sa) el_a(e);
+                }
+                if (copy_stage && slot >= 1 && slot <= NCOPY) copy_part(tcopy, BUF_W, slot - 1);
             }
-            if (copy_stage && k >= 1 && k <= NCOPY) copy_part(tcopy, BUF_W, k - 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (!copy_stage) {                                         // end of a tile's second stage
-            wait_vm_keep<NCOPY>();                                 // tile (s >> 1) + 1 has landed
+        if (!copy_stage) {
+            wait_vm_keep<NCOPY>();
             barrier_lds();
         }
     };
 
-    // Prologue: tiles 0 and 1; tile -1 (buffer 3) zeroed.
     for (int i = tid; i < kTile / 16; i += 64 * NW) {
         lds_store16(Kbuf + 3 * kTile + 16 * i, u32x4{0, 0, 0, 0});
         lds_store16(Vbuf + 3 * kTile + 16 * i, u32x4{0, 0, 0, 0});
@@ -1145,18 +1153,25 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         if (s + 7 < n_stage) stage(std::integral_constant<int, 7>{}, s + 7);
     }
     wait_vm_all();
+    // The accumulators were last written by matrix products issued from inline
+    // assembly, which the compiler does not track: wait them out before reading.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    if (q < N) {
-        uint16_t* dQr = p.dQ + qhead + (size_t)q * D;
 #pragma unroll
-        for (int db = 0; db < NBD; ++db)
+    for (int u = 0; u < U; ++u) {
+        const int q = qu[u];
+        if (q < N) {
+            uint16_t* dQr = p.dQ + qhead + (size_t)q * D;
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int d0 = 32 * db + 8 * rq + 4 * g;
-                *reinterpret_cast<u32x2*>(dQr + d0) =
-                    u32x2{pack_bf16(acc[db][4 * rq] * p.scale, acc[db][4 * rq + 1] * p.scale),
-                          pack_bf16(acc[db][4 * rq + 2] * p.scale, acc[db][4 * rq + 3] * p.scale)};
-            }
+            for (int db = 0; db < NBD; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * db + 8 * rq + 4 * g;
+                    *reinterpret_cast<u32x2*>(dQr + d0) =
+                        u32x2{pack_bf16(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
+                              pack_bf16(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
+                }
+        }
     }
 }
 
@@ -1561,7 +1576,8 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                                    dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
         }
         void* args[] = {&arg};
-        const long grid = (long)p.B * p.Hq * ((p.N + 127) / 128);
+        const int rows_per_wg = D <= 128 ? 256 : 128;
+        const long grid = (long)p.B * p.Hq * ((p.N + rows_per_wg - 1) / rows_per_wg);
         const void* fn;
         if constexpr (D <= 128) fn = reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL>);
         else fn = reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>);
