@@ -920,7 +920,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     constexpr int NCOPY = 2 * PERW;
     constexpr int kPrefetch = 4;
     constexpr int NE = 16 * U;                        // dS elements per lane per block
-    static_assert(NSD == 2 * NQ && PERW >= 1 && NCOPY <= SL, "stage program shape");
+    static_assert(NSD == 2 * NQ && PERW >= 1 && NCOPY <= SL && SL % kPrefetch == 0, "stage program shape");
     __shared__ __attribute__((aligned(256))) char Ka[4 * kTile], Va[4 * kTile];
     FA2_LDS char* const Kbuf = (FA2_LDS char*)Ka;
     FA2_LDS char* const Vbuf = (FA2_LDS char*)Va;
@@ -1026,24 +1026,27 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[1][u][r] = -kInf;
 
+    bf16x8 abuf[kPrefetch];           // operands loaded ahead of their products
     auto stage = [&](auto s8_tag, int s) __attribute__((always_inline)) {
         constexpr int S8 = decltype(s8_tag)::value;
         constexpr int P_SD = S8 & 1;
         constexpr int P_EL = P_SD ^ 1;
         constexpr int BUF_SD = (S8 >> 1) & 3;
         constexpr int BUF_Q = ((S8 >> 1) + 3) & 3;
-        constexpr int OFF_SD = BUF_SD * kTile + 32 * P_SD * RB;
-        constexpr int OFF_Q = BUF_Q * kTile + 32 * P_SD * RB;
-
-        auto load_a = [&](int k) -> bf16x8 {
+        // Operand load k of stage T8 (mod 8): its buffers are compile-time offsets.
+        auto load_at = [&](auto t8_tag, int k) -> bf16x8 {
+            constexpr int T8 = decltype(t8_tag)::value;
+            constexpr int off_sd = ((T8 >> 1) & 3) * kTile + 32 * (T8 & 1) * RB;
+            constexpr int off_q = (((T8 >> 1) + 3) & 3) * kTile + 32 * (T8 & 1) * RB;
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
-                return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + OFF_SD));
+                return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
-            const int off = OFF_Q + 16 * h * RB;
+            const int off = off_q + 16 * h * RB;
             return cat_tr(lds_load_tr(tp1[db] + off), lds_load_tr(tp2[db] + off));
         };
+        auto load_a = [&](int k) { return load_at(s8_tag, k); };
         auto product = [&](int k, int u, bf16x8 a) {
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
@@ -1101,9 +1104,14 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         const bool copy_stage = (S8 & 1) == 0;
         constexpr int BUF_W = ((S8 >> 1) + 2) & 3;
         const int tcopy = (s >> 1) + 2;
-        bf16x8 abuf[kPrefetch];
+        // An even stage and the odd one after it read the same tile (no barrier
+        // between them), so the even stage loads the odd stage's first operands
+        // in its last slots; operand k always goes to abuf[k % kPrefetch].
+        constexpr bool kLoadedBefore = (S8 & 1) == 1;
+        if constexpr (!kLoadedBefore) {
 #pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+            for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+        }
         // 2 * SL product slots: load k feeds slots 2k (u = 0) and 2k + 1 (u = 1).
 #pragma unroll
         for (int k = 0; k < SL; ++k) {
@@ -1113,6 +1121,8 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 const int slot = U * k + u;
                 if (u == 0 && k + kPrefetch < SL) abuf[k % kPrefetch] = load_a(k + kPrefetch);
+                else if (u == 0 && copy_stage)
+                    abuf[k % kPrefetch] = load_at(std::integral_constant<int, S8 + 1>{}, k + kPrefetch - SL);
                 product(k, u, a);
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
