@@ -758,8 +758,8 @@ void bwd_dq_kernel(const BwdParams p) {
     const int level = blockIdx.x / BH;
     const int bh = blockIdx.x - level * BH;
     const int qtile = n_qtiles - 1 - level;
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
     const int hk = hq / p.G;
     const int N = p.N;
     const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
@@ -936,8 +936,8 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     const int level = blockIdx.x / BH;
     const int bh = blockIdx.x - level * BH;
     const int qtile = n_qtiles - 1 - level;
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
     const int hk = hq / p.G;
     const int N = p.N;
     const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
@@ -1031,9 +1031,9 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         constexpr int S8 = decltype(s8_tag)::value;
         constexpr int P_SD = S8 & 1;
         constexpr int P_EL = P_SD ^ 1;
-        constexpr int BUF_SD = (S8 >> 1) & 3;
-        constexpr int BUF_Q = ((S8 >> 1) + 3) & 3;
-        // Operand load k of stage T8 (mod 8): its buffers are compile-time offsets.
+        // Operand load k of stage T8 (mod 8): block T8 lives in tile buffer
+        // (T8 >> 1) & 3, block T8 - 2 in the buffer before it; both at rows
+        // 32 * (T8 & 1).  Every offset is a compile-time immediate.
         auto load_at = [&](auto t8_tag, int k) -> bf16x8 {
             constexpr int T8 = decltype(t8_tag)::value;
             constexpr int off_sd = ((T8 >> 1) & 3) * kTile + 32 * (T8 & 1) * RB;

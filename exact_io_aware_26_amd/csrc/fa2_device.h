@@ -73,6 +73,25 @@ __device__ __forceinline__ float sum_halves(float x) {
     return u32_as_f32(lo) + u32_as_f32(hi);
 }
 
+// Workgroup `idx` of one level of a query-tile grid (B * Hq workgroups per
+// level) -> batch and query head.  Workgroups are dealt round-robin to the 8
+// XCDs, so idx % 8 picks the XCD.  With G > 1 query heads per K/V head and
+// B * Hkv a multiple of 8, the G heads of a K/V head get one residue (and so
+// share one XCD's L2, with every level of those heads); otherwise consecutive
+// ids walk the heads.  Either way the map is a bijection onto [0, B * Hq).
+__device__ __forceinline__ void level_head(int idx, int Hq, int G, int B, int& b, int& hq) {
+    const int Hkv = Hq / G;
+    if (G > 1 && (B * Hkv) % 8 == 0) {
+        const int x = idx & 7, r = idx >> 3;        // XCD and rank on it
+        const int m = r % G, gi = (r / G) * 8 + x;  // head m of K/V head group gi
+        b = gi / Hkv;
+        hq = (gi - b * Hkv) * G + m;
+    } else {
+        b = idx / Hq;
+        hq = idx - b * Hq;
+    }
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte LDS load / store.

@@ -125,8 +125,8 @@ void fwd_kernel(const FwdParams p) {
     const int level = blockIdx.x / BH;
     const int bh = blockIdx.x - level * BH;
     const int qtile = p.n_qtiles - 1 - level;
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
     const int hk = hq / p.G;
     const int N = p.N;
 
@@ -338,8 +338,8 @@ void fwd_pipe_kernel(const FwdParams p) {
     const int level = blockIdx.x / BH;
     const int bh = blockIdx.x - level * BH;
     const int qtile = p.n_qtiles - 1 - level;
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
     const int hk = hq / p.G;
     const int N = p.N;
     const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
