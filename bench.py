@@ -88,6 +88,56 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
     }
 
 
+
+def _median_ms(torch, fn, warmup=20, groups=5, per_group=10):
+    """Median and minimum over `groups` of the mean time per call of `per_group`
+    back-to-back calls (events around each group, on the current stream), after
+    `warmup` calls."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(groups)]
+    for a, b in ev:
+        a.record()
+        for _ in range(per_group):
+            fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / per_group for a, b in ev)
+    return t[len(t) // 2], t[0]
+
+
+def extra_figures(torch, fa2, workloads, dev):
+    """Forward of every throughput configuration, and the backward at their shapes.
+
+    Inputs are iid N(0,1) bf16 drawn on the device from each configuration's seed
+    (the same distribution as the parity inputs; only the generator differs).
+    """
+    out = {}
+    fwd_cfgs = (workloads.SHORT_NONCAUSAL, workloads.SHORT_CAUSAL, workloads.LONG,
+                workloads.GQA_D128, workloads.GQA_D256)
+    bwd_cfgs = (workloads.SHORT_NONCAUSAL, workloads.SHORT_CAUSAL, workloads.GQA_D128, workloads.GQA_D256)
+    for wl in fwd_cfgs:
+        log(f"extra figures: {wl.name}")
+        g = torch.Generator(device=dev).manual_seed(wl.seed)
+        mk = lambda h: torch.randn(wl.B, h, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+        q, k, v = mk(wl.Hq), mk(wl.Hkv), mk(wl.Hkv)
+        o, lse = fa2.forward(q, k, v, causal=wl.causal)
+        med, mn = _median_ms(torch, lambda: fa2.forward(q, k, v, causal=wl.causal, out=o, lse=lse))
+        rec = {"fwd_ms": med, "fwd_ms_min": mn, "fwd_tflops": wl.fwd_flops() / (med * 1e-3) / 1e12}
+        rec["fwd_pct_peak"] = 100 * rec["fwd_tflops"] / PEAK_BF16_TFLOPS
+        if wl in bwd_cfgs:
+            do = mk(wl.Hq)
+            ws = torch.empty(fa2.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d), dtype=torch.uint8, device=dev)
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+            med, mn = _median_ms(torch, lambda: fa2.backward(q, k, v, o, lse, do, causal=wl.causal,
+                                                             workspace=ws, grads=grads))
+            rec.update({"bwd_ms": med, "bwd_ms_min": mn, "bwd_tflops": wl.bwd_flops() / (med * 1e-3) / 1e12})
+            rec["bwd_pct_peak"] = 100 * rec["bwd_tflops"] / PEAK_BF16_TFLOPS
+            del do, ws, grads
+        out[wl.name] = rec
+        del q, k, v, o, lse
+    return out
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +145,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence forward figure")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations' figures")
     ap.add_argument("--probe", action="store_true",
                     help="for profilers: one plain copy of known size, then one forward and each backward "
                          "stage once; prints no JSON")
@@ -207,25 +257,7 @@ def main() -> int:
 
     extra = {}
     if not args.no_extra:
-        wl = workloads.LONG
-        log(f"extra forward figure: {wl.name}")
-        g = torch.Generator(device=dev).manual_seed(wl.seed)
-        ql = torch.randn(wl.B, wl.Hq, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
-        kl = torch.randn(wl.B, wl.Hkv, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
-        vl = torch.randn(wl.B, wl.Hkv, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
-        ol, ll = fa2.forward(ql, kl, vl, causal=wl.causal)
-        for _ in range(3):
-            fa2.forward(ql, kl, vl, causal=wl.causal, out=ol, lse=ll)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            fa2.forward(ql, kl, vl, causal=wl.causal, out=ol, lse=ll)
-        e1.record()
-        torch.cuda.synchronize()
-        lms = e0.elapsed_time(e1) / 10
-        extra[wl.name] = {"fwd_ms": lms, "fwd_tflops": wl.fwd_flops() / (lms * 1e-3) / 1e12,
-                          "fwd_pct_peak": 100 * wl.fwd_flops() / (lms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-        del ql, kl, vl, ol, ll
+        extra = extra_figures(torch, fa2, workloads, dev)
 
     cpu = None
     if args.cpu_budget > 0:

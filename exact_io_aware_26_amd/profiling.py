@@ -11,12 +11,19 @@ traffic, a JSON record that ``bench.py`` reads):
   ``bench.py --probe`` (``FETCH_SIZE``, then ``WRITE_SIZE``, KiB per
   dispatch).  Each counter is scaled by the factor that maps its reading for
   the probe's plain device copy of known size to the true byte count.
+* ``counters``: per kernel (its last, warmed-up dispatch), the matrix-core
+  busy share, the clock, vector instructions per matrix product, LDS bank
+  conflicts and HBM GB/s, from two ``rocprofv3 --kernel-trace --stats --pmc``
+  runs of a short bench (``SQ_*`` counters; durations from the same runs'
+  kernel traces) and the traffic runs.
 
 Usage::
 
     python -m exact_io_aware_26_amd.profiling trace --stats DIR --bench-json FILE --command CMD --out FILE.md
     python -m exact_io_aware_26_amd.profiling traffic --fetch DIR --write DIR --kernel NAME \\
         --copy-bytes N --commands CMD1 CMD2 --out-json FILE.json --out-md FILE.md
+    python -m exact_io_aware_26_amd.profiling counters --pmc DIR_A DIR_B --fetch DIR --write DIR \\
+        --copy-bytes N --commands CMD_A CMD_B --out FILE.md
 """
 from __future__ import annotations
 
@@ -156,6 +163,63 @@ def trace(stats_dir: str, bench_json: str, command: str) -> str:
     return "\n".join(md) + "\n"
 
 
+# MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs; a v_mfma_f32_32x32x16_bf16
+# keeps a SIMD's matrix core busy for 32 clocks (32768 FLOP).
+N_SE, N_SIMD, MFMA_CLOCKS, FLOP_PER_SIMD_CLOCK = 32, 1024, 32, 1024
+
+
+def _durations_us(directory: str) -> dict[str, float]:
+    """Duration of each kernel's last dispatch (the warmed-up one), from the kernel trace."""
+    out: dict[str, float] = {}
+    with open(_one_csv(directory, "*kernel_trace.csv")) as f:
+        for r in sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"])):
+            out[short_name(r["Kernel_Name"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    return out
+
+
+def counters(pmc_dirs: list[str], fetch_dir: str, write_dir: str, copy_bytes: int, commands: list[str]) -> str:
+    vals: dict[str, dict[str, float]] = {}
+    dur: dict[str, float] = {}
+    for d in pmc_dirs:
+        with open(_one_csv(d, "*counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                vals.setdefault(short_name(r["Kernel_Name"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for k, v in _durations_us(d).items():
+            dur.setdefault(k, v)
+    fetch = read_counter(fetch_dir, "FETCH_SIZE")
+    write = read_counter(write_dir, "WRITE_SIZE")
+    ck = [k for k in fetch if COPY_KERNEL in k][0]
+    fs, ws = copy_bytes / (fetch[ck][0] * 1024.0), copy_bytes / (write[ck][0] * 1024.0)
+    md = ["# Matrix-core, vector, LDS and HBM counters per kernel (B4 H16 N8192 d128 causal)", "",
+          "Counter runs; each kernel's last dispatch (counters and duration from the same run):", ""]
+    md += [f"    {c}" for c in commands]
+    md += ["", "Derived per kernel: clock = SQ_BUSY_CYCLES / (32 shader engines x duration); MFMA busy = "
+           "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x clock x duration); the matrix-core peak at that clock is "
+           "1024 SIMDs x clock x 1024 FLOP; VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; "
+           "LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; LDS wait = SQ_WAIT_INST_LDS / "
+           "SQ_WAVE_CYCLES; HBM GB/s = (FETCH_SIZE x %.4f + WRITE_SIZE x %.4f) KiB / duration "
+           "(scales from a plain copy, as in the traffic record)." % (fs, ws), "",
+           "| kernel | us | clock GHz | MFMA busy | VALU per MFMA | LDS bank conflicts | LDS wait | HBM GB/s |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    raw = ["", "Raw counters:", "", "| kernel | counter | value |", "|---|---|---:|"]
+    for name, c in vals.items():
+        if COPY_KERNEL in name or "FillFunctor" in name or name not in dur:
+            continue
+        t = dur[name] * 1e-6
+        clock = c.get("SQ_BUSY_CYCLES", 0.0) / N_SE / t if t else 0.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * clock * t) if clock else 0.0
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        vpm = (c.get("SQ_INSTS_VALU", 0.0) - mf) / mf if mf else float("nan")
+        lds = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"] if c.get("SQ_LDS_IDX_ACTIVE") else 0.0
+        lw = c.get("SQ_WAIT_INST_LDS", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else 0.0
+        hbm = ((fetch.get(name, [0.0])[0] * fs + write.get(name, [0.0])[0] * ws) * 1024.0) / t / 1e9
+        md.append(f"| {name} | {dur[name]:.1f} | {clock / 1e9:.2f} | {100 * busy:.1f} % | {vpm:.2f} | "
+                  f"{100 * lds:.2f} % | {100 * lw:.1f} % | {hbm:.0f} |")
+        for cn in sorted(c):
+            raw.append(f"| {name} | {cn} | {c[cn]:.6g} |")
+    return "\n".join(md + raw) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -172,7 +236,18 @@ def main() -> None:
     x.add_argument("--commands", nargs="+", required=True)
     x.add_argument("--out-json", required=True)
     x.add_argument("--out-md", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--commands", nargs="+", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.what == "counters":
+        with open(a.out, "w") as f:
+            f.write(counters(a.pmc, a.fetch, a.write, a.copy_bytes, a.commands))
+        return
     if a.what == "trace":
         with open(a.out, "w") as f:
             f.write(trace(a.stats, a.bench_json, a.command))

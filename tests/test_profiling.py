@@ -64,3 +64,41 @@ def test_source_digest_ignores_comments_and_layout():
     c = "int f(int x) { return x + 2; }"
     assert profiling._code_only(a) == profiling._code_only(b)
     assert profiling._code_only(b) != profiling._code_only(c)
+
+
+def _write_trace(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for name, ns in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + ns})
+            t += ns + 1000
+
+
+def test_counters_derive_clock_and_mfma_busy(tmp_path):
+    a, b = tmp_path / "a", tmp_path / "b"
+    t_ns = 1_000_000                                   # 1 ms
+    clock = 2.0e9
+    busy_cycles = profiling.N_SE * clock * 1e-3        # all shader engines busy for the whole launch
+    mfma = 1000.0
+    for d, cvals in ((a, {"SQ_BUSY_CYCLES": busy_cycles, "SQ_VALU_MFMA_BUSY_CYCLES":
+                          0.5 * profiling.N_SIMD * clock * 1e-3, "SQ_INSTS_MFMA": mfma,
+                          "SQ_INSTS_VALU": 4 * mfma, "SQ_WAVE_CYCLES": 100.0}),
+                     (b, {"SQ_LDS_BANK_CONFLICT": 1.0, "SQ_LDS_IDX_ACTIVE": 100.0, "SQ_WAIT_INST_LDS": 10.0})):
+        os.makedirs(d, exist_ok=True)
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for cn, v in cvals.items():
+                w.writerow({"Kernel_Name": KV, "Counter_Name": cn, "Counter_Value": v})
+        _write_trace(d, [(KV, 5 * t_ns), (KV, t_ns)])   # a cold dispatch, then the one reported
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [(COPY, 512.0), (KV, 1024.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [(COPY, 1024.0), (KV, 0.0)])
+    md = profiling.counters([str(a), str(b)], str(tmp_path / "f"), str(tmp_path / "w"), 1 << 20, ["c1", "c2"])
+    row = [l for l in md.splitlines() if l.startswith("| bwd_kv_kernel") and "SQ_" not in l][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "1000.0" and cells[2] == "2.00" and cells[3] == "50.0 %" and cells[4] == "3.00"
+    assert cells[5] == "1.00 %" and cells[6] == "10.0 %"
+    assert cells[7] == "2"                              # 1024 KiB x 2.0 read in 1 ms = 2.1 GB/s
