@@ -1524,6 +1524,341 @@ void bwd_kv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// bwd_kv256: the K/V-tile loop for d = 256 (dQ in its own pass), the d = 128
+// design split over the head dim: a pair of workgroups shares each 128-key
+// tile, both computing s = Q K^T and dp = dO V^T over all 256 dims (K and V of
+// the wave's keys as register operands), each accumulating dK and dV for 128
+// of the columns.  That costs the s and dp products twice, but the whole K/V
+// rows and 128 columns of both accumulators (held in AGPRs) fit one wave's
+// registers.  64-row query tiles (Q, dO: 32 KiB each) are copied two deep.
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_kv256_kernel(const BwdParams p) {
+    constexpr int D = 256, DH = 128;          // head dim; dK / dV columns per workgroup
+    constexpr int NW = 4, BC = 32 * NW, BR = kBwdRowPad;
+    constexpr int RB = 2 * D;                 // bytes per row of the Q / dO tiles
+    constexpr int kTile = BR * RB;
+    constexpr int KSD = D / 16;               // reduction steps over the head dim
+    constexpr int NBD = DH / 32;              // 32-wide blocks of this workgroup's dK / dV columns
+    constexpr int RPI = 1024 / RB;            // tile rows per wave copy instruction
+    constexpr int CPR = RB / 16;              // 16-byte chunks per row
+    constexpr int PERW = kTile / 1024 / NW;   // copy instructions per wave per tensor
+    static_assert(BR == 64 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    // Two LDS arrays of one query tile each, [Q | dO | L log2 e | -D], 512-byte
+    // aligned: every read of a tile is a per-tile lane base (with the array's
+    // address folded in) XOR a constant, plus an immediate offset below 64 KiB.
+    constexpr int kBuf = 2 * kTile + 2 * BR * 4;
+    static_assert(kBuf % 512 == 0, "tile arrays keep the 512-byte alignment the column XOR needs");
+    __shared__ __attribute__((aligned(512))) char Ta0[kBuf], Ta1[kBuf];
+    FA2_LDS char* const T0 = (FA2_LDS char*)Ta0;
+    FA2_LDS char* const T1 = (FA2_LDS char*)Ta1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    // Workgroup pairs (ids 2i, 2i + 1) share a key tile: columns [0, 128) and
+    // [128, 256) of its dK and dV.
+    const int half = blockIdx.x & 1;
+    const int wg = blockIdx.x >> 1;
+    const int BHk = p.B * p.Hkv;
+    const int kvtile = wg / BHk;
+    const int bh = wg - kvtile * BHk;
+    const int b = bh / p.Hkv;
+    const int hk = bh - b * p.Hkv;
+    const int N = p.N;
+    const int kv0 = kvtile * BC;
+    const int kw0 = kv0 + 32 * wave;
+    const int kv = kw0 + li;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+
+    bf16x8 kf[KSD], vf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+        if (kv < N) {
+            kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
+            vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
+        }
+        kf[ks] = as_bf16x8(kx);
+        vf[ks] = as_bf16x8(vx);
+    }
+    f32x16 dv[NBD], dk[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) {
+        dv[i] = zero16();
+        dk[i] = zero16();
+    }
+
+    // Query tiles: for each of the G query heads sharing this K/V head, the
+    // 64-row tiles from the first one the causal mask lets through.
+    const int n_qt = (N + BR - 1) / BR;
+    const int i_begin = CAUSAL ? kv0 / BR : 0;
+    const int n_i = n_qt - i_begin;
+    const int n_iter = n_i * p.G;
+
+    // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
+    // tile program spreads over its first slots: Q and dO rows
+    // (clamped to N-1 past the end; those rows have L = +inf, so P = dS = 0),
+    // and the padded L log2 e and -D rows (waves 0 and 2 both copy L, 1 and 3
+    // both copy -D: identical bytes, so every wave issues the same number of
+    // copies).
+    constexpr int NCOPY = 2 * PERW + 1;
+    struct TileCopy {
+        const char* qbase;
+        const char* obase;
+        const float* ld_src;
+        int last, lr, lc;
+        FA2_LDS char* T;
+    };
+    auto plan_copy = [&](int it, FA2_LDS char* T) {
+        const int hq = hk * p.G + it / n_i;
+        const int qt0 = (i_begin + it % n_i) * BR;
+        const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
+        const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
+        TileCopy c;
+        c.qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
+        c.obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
+        c.ld_src = (wave & 1) ? p.Dneg + prow : p.L2 + prow;
+        c.last = N - 1 - qt0;
+        c.lr = lane / CPR;
+        c.lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
+        asm volatile("" : "+v"(c.lr), "+v"(c.lc));   // rebuilt per tile instead of held across the loop
+        c.T = T;
+        return c;
+    };
+    auto copy_part = [&](const TileCopy& c, int j) {
+        if (j < 2 * PERW) {
+            const int i = j % PERW;
+            const int R = (wave * PERW + i) * RPI;
+            const uint32_t off = (uint32_t)(min(R + c.lr, c.last) * RB + (c.lc ^ (16 * swz<RB>(R))));
+            if (j < PERW) copy_to_lds16(c.qbase, off, c.T + (wave * PERW + i) * 1024);
+            else copy_to_lds16(c.obase, off, c.T + kTile + (wave * PERW + i) * 1024);
+        } else {
+            copy_to_lds4(c.ld_src, 4 * lane, c.T + 2 * kTile + (wave & 1) * BR * 4);
+        }
+    };
+    auto copy_tile = [&](int it, FA2_LDS char* T) {
+        const TileCopy c = plan_copy(it, T);
+#pragma unroll
+        for (int j = 0; j < NCOPY; ++j) copy_part(c, j);
+    };
+
+    // LDS operand addresses: the swizzle only flips bits 4.. of a row's byte
+    // offset below RB, so they are a per-lane base XOR a constant (32*ks for
+    // Q / dO rows, chunk 2*ks + g; 64*db for the transposed reads).
+    const int j16 = lane & 15;
+    const int xq = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+    const int kb_lane = li * RB + 16 * (g ^ swz<RB>(li));
+    // Transposed reads address this workgroup's half of the columns (bit 8 of a
+    // 512-byte row).
+    const int vb1_lane = (r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1))) ^ (256 * half);
+    const int vb2_lane = (r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2))) ^ (256 * half);
+
+    // One query tile as a fixed program of matrix products, one per slot
+    // (NS = 2 * D/16 products of s and dp per 32-row block, NG = 4 * D/32 of
+    // dV and dK; 16, 16 for d = 128):
+    //   s, dp of block 0          (A: Q / dO rows, B: K / V of this lane)
+    //   s, dp of block 1          | P, dS of block 0, 16 / NS elements per slot
+    //   dV, dK over block 0       | P, dS of block 1, 16 / NG elements per slot
+    //   dV, dK over block 1
+    // Each product's A operand is read from LDS kPrefetch slots ahead; a
+    // scheduling fence between slots keeps this order, so the compiler waits
+    // only for the read a product needs.
+    constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = 2 * NS + 2 * NG;
+    constexpr int kPrefetch = 3;                    // 4 would spill here (512 registers)
+    static_assert(NS >= 16 && NG >= 16, "slot program shape");
+    static_assert(NCOPY <= NP, "the copies of the next tile fit in one tile program");
+    auto tile = [&](const FA2_LDS char* T, int qt0, const TileCopy& cp) {
+        // Lane bases with the tile's address folded in, rebuilt per tile (opaque
+        // to the compiler) rather than held across the loop.
+        const uint32_t tb = (uint32_t)(uintptr_t)T;
+        uint32_t kb = tb + kb_lane, vb1 = tb + vb1_lane, vb2 = tb + vb2_lane, lb = tb + 2 * kTile + 16 * g;
+        asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2), "+v"(lb));
+        auto at = [](uint32_t a) { return (const FA2_LDS char*)(uintptr_t)a; };
+        // Four consecutive floats of the L log2 e (which = 0) or -D (which = 1)
+        // rows: queries 32 * blk + 8 * rl + 4g .. +3, the order of a score
+        // accumulator's registers 4 rl .. 4 rl + 3.
+        auto ld_rows = [&](int which, int blk, int rl) {
+            return *reinterpret_cast<const FA2_LDS f32x4*>(at(lb) + 4 * (which * BR + 32 * blk + 8 * rl));
+        };
+        f32x16 sc[2], dpc[2];
+        uint32_t pp[2][8], pd[2][8];
+        f32x4 lv[2][4];
+        f32x16 nd[2];                        // -D of each block: where its dP products start
+        auto load_nd = [&](int blk, int rl) {
+            const f32x4 v = ld_rows(1, blk, rl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
+        };
+        // A operand of product k.
+        auto load_a = [&](int k) -> bf16x8 {
+            if (k < 2 * NS) {
+                const int blk = k / NS, ks = (k % NS) >> 1;
+                const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
+                return as_bf16x8(lds_load16(at(kb ^ (32 * ks)) + off));
+            }
+            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
+            return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
+        };
+        auto product = [&](int k, bf16x8 a) {
+            if (k < 2 * NS) {
+                const int blk = k / NS, ks = (k % NS) >> 1;
+                if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
+                else sc[blk] = mfma32(a, kf[ks], ks == 0 ? zero16() : sc[blk]);
+                return;
+            }
+            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            // Issued as assembly to keep the accumulators in AGPRs (with the
+            // whole head dim of K and V as operands they do not fit in VGPRs).
+            if (jj & 1) {
+                const bf16x8 bs = as_bf16x8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
+                f32x16 c = dk[db];
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bs));
+                dk[db] = c;
+            } else {
+                const bf16x8 bp = as_bf16x8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
+                f32x16 c = dv[db];
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bp));
+                dv[db] = c;
+            }
+        };
+        // Element r of P and dS of block blk (query 8*(r/4) + 4g + r%4 of the
+        // block, this lane's key) in three stages -- c*s - L log2 e, exp2, then
+        // dS and the bf16 packing -- run for elements r, r-1, r-2 in one slot,
+        // so the instructions of a slot do not wait on each other.
+        // Each stage's result is pinned in its slot (an empty asm that redefines
+        // it), or the compiler sinks the arithmetic down to the dV / dK products
+        // that consume it and the slots before those get no vector work.
+        auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+        auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
+        auto stage_a = [&](int blk, int r) {
+            float x = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]);
+            pin(x);
+            sc[blk][r] = x;
+        };
+        auto stage_b = [&](int blk, int r) {
+            float x = exp2_fast(sc[blk][r]);
+            pin(x);
+            sc[blk][r] = x;
+        };
+        auto stage_c = [&](int blk, int r) {
+            const float pr = sc[blk][r];
+            float ds = pr * dpc[blk][r];
+            pin(ds);
+            dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
+            if (r & 1) {
+                uint32_t a = pack_bf16(sc[blk][r - 1], pr), c = pack_bf16(dpc[blk][r - 1], ds);
+                pin_u(a);
+                pin_u(c);
+                pp[blk][r >> 1] = a;
+                pd[blk][r >> 1] = c;
+            }
+        };
+        // Vector work of slot k: L of a block is read half a block of products
+        // before its P, -D of block 1 with L of block 0; then the staged elements.
+        auto vector_work = [&](int k) {
+            const int rl = k - NS / 2;                        // slots NS/2 .. NS/2+3
+            if (rl >= 0 && rl < 4) {
+                lv[0][rl] = ld_rows(0, 0, rl);
+                load_nd(1, rl);
+            }
+            const int rl1 = k - (NS + NS / 2);                // block 1's L
+            if (rl1 >= 0 && rl1 < 4) lv[1][rl1] = ld_rows(0, 1, rl1);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int start = blk ? 2 * NS : NS;          // first slot of the block's elements
+                const int S = blk ? NG : NS;                  // slots of the phase they run in
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {                // element r starts at slot r * S / 16
+                    const int t = k - start - r * S / 16;
+                    if (t == 2) stage_c(blk, r);
+                    if (t == 1) stage_b(blk, r);
+                    if (t == 0) stage_a(blk, r);
+                }
+            }
+        };
+        // Causal mask of block blk, once its scores are complete: only a block
+        // that starts below this wave's last key has keys above the diagonal
+        // (one or two blocks per query head in a wave's whole loop).
+        auto mask = [&](int blk) {
+            if (CAUSAL && qt0 + 32 * blk < kw0 + 31) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk][i] = -kInf;
+            }
+        };
+        // -D of block 0 before the first operands: its dP products start at slot 1.
+#pragma unroll
+        for (int rl = 0; rl < 4; ++rl) load_nd(0, rl);
+        bf16x8 abuf[kPrefetch];
+        auto slot = [&](int k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 a = abuf[k % kPrefetch];
+            if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
+            product(k, a);
+            vector_work(k);
+            if (k < NCOPY) copy_part(cp, k);                // the next tile's copies: first slots
+        };
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) slot(k);
+        mask(0);
+#pragma unroll
+        for (int k = NS; k < 2 * NS; ++k) slot(k);
+        mask(1);
+#pragma unroll
+        for (int k = 2 * NS; k < NP; ++k) slot(k);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
+        // The other buffer was released by the barrier ending the previous
+        // step.  Copies past the last tile repeat it into it (never read).
+        tile(T, (i_begin + it % n_i) * BR, plan_copy(min(it + 1, n_iter - 1), Tw));
+        wait_vm_all();                  // tile it+1 has landed
+        barrier_lds();
+    };
+
+    if (n_iter > 0) {
+        copy_tile(0, T0);
+        wait_vm_all();
+        __syncthreads();
+        for (int it = 0; it < n_iter; it += 2) {
+            step(it, T0, T1);
+            if (it + 1 < n_iter) step(it + 1, T1, T0);
+        }
+        wait_vm_all();
+    }
+    // The accumulators were last written by matrix products issued from inline
+    // assembly, which the compiler does not track: wait them out before reading.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // epilogue: this lane's key, the whole head dim
+    if (kv < N) {
+        uint16_t* dVr = p.dV + khead + (size_t)kv * D;
+        uint16_t* dKr = p.dK + khead + (size_t)kv * D;
+#pragma unroll
+        for (int db = 0; db < NBD; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d0 = DH * half + 32 * db + 8 * rq + 4 * g;
+                *reinterpret_cast<u32x2*>(dVr + d0) =
+                    u32x2{pack_bf16(dv[db][4 * rq], dv[db][4 * rq + 1]),
+                          pack_bf16(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
+                *reinterpret_cast<u32x2*>(dKr + d0) =
+                    u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
+                          pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // dQ = bf16(scale * accumulator), 8 elements per thread.
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const BwdParams p, long n8) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -1568,12 +1903,15 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 threads = 256;
             }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
-        } else {
-            fn = atomic_dq ? reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>)
-                           : reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, false>);
+        } else if (atomic_dq) {
+            fn = reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>);
             constexpr int BC = BwdCfg<D>::BC;
             grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
             threads = 64 * BwdCfg<D>::NW;
+        } else {
+            fn = reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL>);
+            grid = 2L * p.B * p.Hkv * ((p.N + 127) / 128);       // two column halves per key tile
+            threads = 256;
         }
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
         if (e != hipSuccess) return e;
