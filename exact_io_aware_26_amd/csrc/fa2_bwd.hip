@@ -22,8 +22,11 @@
 //   bwd_dq_pipe      d = 64, 128: one workgroup per 256 query rows; dQ stays in
 //                    registers over all key blocks, recomputing S and dP, so no
 //                    atomics are needed and dQ is deterministic.
-//   bwd_main         d = 256: the K/V loop with register-staged tiles; with
-//   bwd_dq           atomic dQ or followed by bwd_dq (the d = 256 dQ pass).
+//   bwd_kv256        d = 256: the K/V loop split over the head dim (two
+//                    workgroups per 128-key tile, 128 columns of dK, dV each).
+//   bwd_dq256        d = 256: the dQ pass with 32-key tiles.
+//   bwd_main         d = 256 in the atomic mode: the K/V loop with
+//                    register-staged tiles and atomically added dQ.
 //   bwd_pair         the pages' atomic accumulation of dQ for d = 64, 128
 //   bwd_dq_convert   (FA2_BWD_DQ_ATOMIC), then dQ = bf16(scale * accumulator).
 //
@@ -717,172 +720,6 @@ void bwd_pair_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// bwd_dq: dQ without atomics for d = 256 (d = 64 and 128 use bwd_dq_pipe
-// below), one workgroup per 128 query rows (4 waves x 32).
-//
-// The dQ contribution of every K/V tile is summed in registers instead of
-// through global atomics: each wave keeps its query rows (Q and dO as MFMA
-// operands, L and D as one value per lane) and streams K/V tiles through
-// double-buffered LDS, recomputing what it needs, all transposed so that
-// each lane owns one query row:
-//     S^T  = K Q^T,   P^T = exp2(c S^T - L log2 e)          (masked on the diagonal)
-//     dP^T = V dO^T,  dS^T = P^T o (dP^T - D)
-//     dQ^T += K^T dS^T          (K^T by transposed LDS reads, dS^T from registers)
-// and finally writes dQ = bf16(scale * dQ) once.  This costs the S and dP
-// products a second time, and in exchange the result is deterministic.
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
-void bwd_dq_kernel(const BwdParams p) {
-    constexpr int BC = D == 256 ? 32 : 64, BRQ = 128, NT = 256;
-    constexpr int RB_D = 2 * D;
-    constexpr int NBS = BC / 32;       // 32-key blocks per tile
-    constexpr int KSD = D / 16;
-    constexpr int NBD = D / 32;
-    constexpr int kTileBytes = BC * RB_D;
-    // Two K/V buffers as four distinct LDS objects: with the loop unrolled by
-    // two, every read names a buffer that differs from the one the in-flight
-    // tile is written to, so the compiler adds no wait on that tile before the
-    // transposed reads of the current one.
-    __shared__ __attribute__((aligned(16))) char K0[kTileBytes], V0[kTileBytes], K1[kTileBytes], V1[kTileBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int g = lane >> 5;
-    const int li = lane & 31;
-
-    // Heaviest causal query tiles first; heads of one level on consecutive ids.
-    const int n_qtiles = (p.N + BRQ - 1) / BRQ;
-    const int BH = p.B * p.Hq;
-    const int level = blockIdx.x / BH;
-    const int bh = blockIdx.x - level * BH;
-    const int qtile = n_qtiles - 1 - level;
-    int b, hq;
-    level_head(bh, p.Hq, p.G, p.B, b, hq);
-    const int hk = hq / p.G;
-    const int N = p.N;
-    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
-    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
-    const uint16_t* Kh = p.K + khead;
-    const uint16_t* Vh = p.V + khead;
-    const int q0 = qtile * BRQ;
-    const int wq0 = q0 + 32 * wave;
-    const int q = wq0 + li;
-    const bool wave_live = wq0 < N;
-
-    bf16x8 qf[KSD], of[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-        if (q < N) {
-            a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
-            c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
-        }
-        qf[ks] = as_bf16x8(a);
-        of[ks] = as_bf16x8(c);
-    }
-    const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
-    const float l2 = q < N ? p.L2[row] : kInf;   // rows past the end: P = 0
-    const float dq_d = q < N ? -p.Dneg[row] : 0.f;
-
-    int n_kv = (N + BC - 1) / BC;
-    if (CAUSAL) n_kv = (min(q0 + BRQ, N) - 1) / BC + 1;
-
-    // K/V tiles go straight from global memory into LDS (global_load_lds_dwordx4):
-    // one wave instruction fills 1 KiB, lane i writing bytes 16*i.., so lane i
-    // fetches the logical chunk that the swizzle assigns to its LDS slot.  Rows
-    // past the end are clamped to row N-1; their keys are masked (P = 0, dS = 0).
-    constexpr int RPI = 1024 / RB_D;               // tile rows per wave instruction
-    constexpr int CPR = RB_D / 16;                 // 16-byte chunks per row
-    constexpr int PERW = kTileBytes / 1024 / (NT / 64);
-    static_assert(PERW >= 1 && kTileBytes % (1024 * (NT / 64)) == 0, "tile / waves mismatch");
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto load = [&](int kv0, FA2_LDS char* Ks, FA2_LDS char* Vs) {
-        const char* Kt = reinterpret_cast<const char*>(Kh + (size_t)kv0 * D);   // uniform tile bases
-        const char* Vt = reinterpret_cast<const char*>(Vh + (size_t)kv0 * D);
-        const int last = N - 1 - kv0;
-        int lr = lane / CPR, ls = lane % CPR;
-        asm volatile("" : "+v"(lr), "+v"(ls));   // rebuilt per tile instead of held across the loop
-#pragma unroll
-        for (int i = 0; i < PERW; ++i) {
-            const int r = (wave_u * PERW + i) * RPI + lr;
-            const uint32_t off = (uint32_t)(min(r, last) * RB_D + 16 * (ls ^ swz<RB_D>(r)));
-            const int dst = (wave_u * PERW + i) * 1024;
-            copy_to_lds16(Kt, off, Ks + dst);
-            copy_to_lds16(Vt, off, Vs + dst);
-        }
-    };
-
-    f32x16 acc[NBD];
-#pragma unroll
-    for (int i = 0; i < NBD; ++i) acc[i] = zero16();
-
-    auto step = [&](int j, FA2_LDS char* Ks, FA2_LDS char* Vs, FA2_LDS char* Kn, FA2_LDS char* Vn)
-                    __attribute__((always_inline)) {
-        const int kv0 = j * BC;
-        if (j + 1 < n_kv) load(kv0 + BC, Kn, Vn);   // the other buffer was released by the last barrier
-        if (wave_live && !(CAUSAL && kv0 > wq0 + 31)) {
-            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
-#pragma unroll
-            for (int bs = 0; bs < NBS; ++bs) {          // one 32-key block at a time
-                f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    s = mfma32(row_operand<RB_D>(Ks, 32 * bs, 16 * ks, lane), qf[ks], s);
-                    dp = mfma32(row_operand<RB_D>(Vs, 32 * bs, 16 * ks, lane), of[ks], dp);
-                }
-                if (need_mask) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if ((CAUSAL && kv > q) || kv >= N) s[r] = -kInf;
-                    }
-                }
-                uint32_t dsp[8];
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = exp2_fast(fmaf(s[r], p.c, -l2));
-                    const float p1 = exp2_fast(fmaf(s[r + 1], p.c, -l2));
-                    dsp[r >> 1] = pack_bf16(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int kk = 2 * bs + hh;
-                    const bf16x8 bds = as_bf16x8(u32x4{dsp[4 * hh], dsp[4 * hh + 1], dsp[4 * hh + 2], dsp[4 * hh + 3]});
-#pragma unroll
-                    for (int db = 0; db < NBD; ++db)
-                        acc[db] = mfma32(tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane), bds, acc[db]);
-                }
-            }
-        }
-        wait_vm_all();             // the next tile has landed in LDS ...
-        __syncthreads();           // ... for every wave, and this one is free
-    };
-
-    load(0, (FA2_LDS char*)K0, (FA2_LDS char*)V0);
-    wait_vm_all();
-    __syncthreads();
-    for (int j = 0; j < n_kv; j += 2) {
-        step(j, (FA2_LDS char*)K0, (FA2_LDS char*)V0, (FA2_LDS char*)K1, (FA2_LDS char*)V1);
-        if (j + 1 < n_kv) step(j + 1, (FA2_LDS char*)K1, (FA2_LDS char*)V1, (FA2_LDS char*)K0, (FA2_LDS char*)V0);
-    }
-
-    if (wave_live && q < N) {
-        uint16_t* dQr = p.dQ + qhead + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NBD; ++db)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int d0 = 32 * db + 8 * rq + 4 * g;
-                *reinterpret_cast<u32x2*>(dQr + d0) =
-                    u32x2{pack_bf16(acc[db][4 * rq] * p.scale, acc[db][4 * rq + 1] * p.scale),
-                          pack_bf16(acc[db][4 * rq + 2] * p.scale, acc[db][4 * rq + 3] * p.scale)};
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
 // bwd_dq_pipe: the dQ pass for d = 64 and 128.
 //
 // One workgroup = 4 wave64s, one wave per SIMD; each wave owns two 32-row query
@@ -1161,6 +998,278 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         if (s + 5 < n_stage) stage(std::integral_constant<int, 5>{}, s + 5);
         if (s + 6 < n_stage) stage(std::integral_constant<int, 6>{}, s + 6);
         if (s + 7 < n_stage) stage(std::integral_constant<int, 7>{}, s + 7);
+    }
+    wait_vm_all();
+    // The accumulators were last written by matrix products issued from inline
+    // assembly, which the compiler does not track: wait them out before reading.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = qu[u];
+        if (q < N) {
+            uint16_t* dQr = p.dQ + qhead + (size_t)q * D;
+#pragma unroll
+            for (int db = 0; db < NBD; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * db + 8 * rq + 4 * g;
+                    *reinterpret_cast<u32x2*>(dQr + d0) =
+                        u32x2{pack_bf16(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
+                              pack_bf16(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bwd_dq256: the pipelined dQ pass at d = 256.  One 32-row query block per
+// wave (128 rows per workgroup); 32-key tiles of K and V (16 KiB each) copied
+// into LDS four deep, one tile per stage, one barrier per stage.  Stage s runs
+// the same program as bwd_dq_pipe's: the s, dp products of block s alternate
+// with the dQ products of block s - 2, while the dS of block s - 1 is formed
+// beside them.  The dQ^T accumulators and the Q / dO operands fill the AGPRs.
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq256_kernel(const BwdParams p) {
+    constexpr int D = 256;
+    constexpr int NW = 4, U = 1, BRQ = 32 * U * NW, BT = 32;   // one 32-key block per tile
+    constexpr int RB = 2 * D;
+    constexpr int kTile = BT * RB;
+    constexpr int KSD = D / 16, NBD = D / 32;
+    constexpr int NSD = 2 * KSD;                      // s, dp operand loads per block
+    constexpr int NQ = 2 * NBD;                       // dQ operand loads per block
+    constexpr int SL = NSD + NQ;                      // operand loads (pairs of products) per stage
+    constexpr int RPI = 1024 / RB, CPR = RB / 16;
+    constexpr int PERW = kTile / 1024 / NW;
+    constexpr int NCOPY = 2 * PERW;
+    constexpr int kPrefetch = 4;
+    constexpr int NE = 16 * U;                        // dS elements per lane per block
+    static_assert(NSD == 2 * NQ && PERW >= 1 && NCOPY <= SL, "stage program shape");
+    __shared__ __attribute__((aligned(256))) char Ka[4 * kTile], Va[4 * kTile];
+    FA2_LDS char* const Kbuf = (FA2_LDS char*)Ka;
+    FA2_LDS char* const Vbuf = (FA2_LDS char*)Va;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    const int n_qtiles = (p.N + BRQ - 1) / BRQ;
+    const int BH = p.B * p.Hq;
+    const int level = blockIdx.x / BH;
+    const int bh = blockIdx.x - level * BH;
+    const int qtile = n_qtiles - 1 - level;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
+    const int hk = hq / p.G;
+    const int N = p.N;
+    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+    const int q0 = qtile * BRQ;
+    const int wq0 = q0 + 32 * U * wave;
+
+    bf16x8 qf[U][KSD], of[U][KSD];
+    float l2[U], dq_d[U];
+    int qu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = wq0 + 32 * u + li;
+        qu[u] = q;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+            if (q < N) {
+                a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
+                c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
+            }
+            qf[u][ks] = as_bf16x8(a);
+            of[u][ks] = as_bf16x8(c);
+        }
+        const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
+        l2[u] = q < N ? p.L2[row] : kInf;
+        dq_d[u] = q < N ? -p.Dneg[row] : 0.f;
+    }
+
+    const int n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
+    const int n_t = n_kb;
+
+    auto copy_part = [&](int t, int buf, int j) {
+        const int kv0 = min(t, n_t - 1) * BT;
+        const int last = N - 1 - kv0;
+        const int i = j % PERW;
+        const int R = (wave * PERW + i) * RPI;
+        const int lr = lane / CPR;
+        const int lc = 16 * ((lane % CPR) ^ swz<RB>(lane / CPR));
+        const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<RB>(R))));
+        const uint16_t* src = (j < PERW ? p.K : p.V) + khead + (size_t)kv0 * D;
+        copy_to_lds16(src, off, (j < PERW ? Kbuf : Vbuf) + buf * kTile + (wave * PERW + i) * 1024);
+    };
+
+    const int j16 = lane & 15;
+    const int xq = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+    const int kb_lane = li * RB + 16 * (g ^ swz<RB>(li));
+    const int vb1_lane = r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1));
+    const int vb2_lane = r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2));
+    const FA2_LDS char* kp[KSD];
+    const FA2_LDS char* vp[KSD];
+    const FA2_LDS char* tp1[NBD];
+    const FA2_LDS char* tp2[NBD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        kp[ks] = Kbuf + (kb_lane ^ (32 * ks));
+        vp[ks] = Vbuf + (kb_lane ^ (32 * ks));
+        asm volatile("" : "+v"(kp[ks]), "+v"(vp[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < NBD; ++db) {
+        tp1[db] = Kbuf + (vb1_lane ^ (64 * db));
+        tp2[db] = Kbuf + (vb2_lane ^ (64 * db));
+        asm volatile("" : "+v"(tp1[db]), "+v"(tp2[db]));
+    }
+
+    f32x16 acc[U][NBD];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < NBD; ++i) acc[u][i] = zero16();
+    f32x16 sc[2][U], dpc[2][U];
+    uint32_t dsp[2][U][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            sc[i][u] = zero16();
+            dpc[i][u] = zero16();
+#pragma unroll
+            for (int r = 0; r < 8; ++r) dsp[i][u][r] = 0u;
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[1][u][r] = -kInf;
+
+    bf16x8 abuf[kPrefetch];           // operands loaded ahead of their products
+    auto stage = [&](auto s4_tag, int s) __attribute__((always_inline)) {
+        constexpr int S4 = decltype(s4_tag)::value;
+        constexpr int P_SD = S4 & 1;
+        constexpr int P_EL = P_SD ^ 1;
+        // Operand load k of stage S4 (mod 4): block S4 is tile buffer S4, block
+        // S4 - 2 the buffer two before it.  Every offset is a compile-time
+        // immediate.
+        auto load_a = [&](int k) -> bf16x8 {
+            constexpr int off_sd = (S4 & 3) * kTile;
+            constexpr int off_q = ((S4 + 2) & 3) * kTile;
+            if (k % 3 != 2) {
+                const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
+                return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
+            }
+            const int qq = k / 3, h = qq / NBD, db = qq % NBD;
+            const int off = off_q + 16 * h * RB;
+            return cat_tr(lds_load_tr(tp1[db] + off), lds_load_tr(tp2[db] + off));
+        };
+        auto product = [&](int k, int u, bf16x8 a) {
+            if (k % 3 != 2) {
+                const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
+                if (j & 1) dpc[P_SD][u] = mfma32(a, of[u][ks], ks == 0 ? zero16() : dpc[P_SD][u]);
+                else sc[P_SD][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : sc[P_SD][u]);
+                return;
+            }
+            const int qq = k / 3, h = qq / NBD, db = qq % NBD;
+            const bf16x8 bds = as_bf16x8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
+                                               dsp[P_SD][u][4 * h + 2], dsp[P_SD][u][4 * h + 3]});
+            // Issued as assembly to keep the accumulator in AGPRs (the compiler
+            // places every builtin product's result in VGPRs here, which would
+            // not fit); acc[u][db] is next touched a dozen products later.
+            f32x16 c = acc[u][db];
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
+            acc[u][db] = c;
+        };
+        auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+        auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
+        auto el_a = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = fmaf(sc[P_EL][u][r], p.c, -l2[u]);
+            pin(x);
+            sc[P_EL][u][r] = x;
+        };
+        auto el_b = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = exp2_fast(sc[P_EL][u][r]);
+            pin(x);
+            sc[P_EL][u][r] = x;
+        };
+        auto el_c = [&](int e) {
+            const int u = e >> 4, r = e & 15;
+            float x = sc[P_EL][u][r] * (dpc[P_EL][u][r] - dq_d[u]);
+            pin(x);
+            dpc[P_EL][u][r] = x;
+            if (r & 1) {
+                uint32_t w = pack_bf16(dpc[P_EL][u][r - 1], x);
+                pin_u(w);
+                dsp[P_EL][u][r >> 1] = w;
+            }
+        };
+        {
+            const int kb0 = 32 * (s - 1);
+            if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                        if ((CAUSAL && key > qu[u]) || key >= N) sc[P_EL][u][i] = -kInf;
+                    }
+            }
+        }
+        // Each stage copies the next tile into the buffer that the barrier
+        // ending the previous stage released (block s - 3's).
+        constexpr int BUF_W = (S4 + 1) & 3;
+        const int tcopy = s + 1;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+        // 2 * SL product slots: load k feeds slots 2k (u = 0) and 2k + 1 (u = 1).
+#pragma unroll
+        for (int k = 0; k < SL; ++k) {
+            const bf16x8 a = abuf[k % kPrefetch];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int slot = U * k + u;
+                if (u == 0 && k + kPrefetch < SL) abuf[k % kPrefetch] = load_a(k + kPrefetch);
+                product(k, u, a);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    const int sa = e * (U * SL - 3) / (NE - 1);
+                    if (slot == sa + 2) el_c(e);
+                    if (slot == sa + 1) el_b(e);
+                    if (slot == sa) el_a(e);
+                }
+                if (slot >= 1 && slot <= NCOPY) copy_part(tcopy, BUF_W, slot - 1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_all();                                    // tile s + 1 has landed
+        barrier_lds();
+    };
+
+    // Prologue: tile 0; the buffers of tiles -2 and -1 zeroed.
+    for (int i = tid; i < 2 * kTile / 16; i += 64 * NW) {
+        lds_store16(Kbuf + 2 * kTile + 16 * i, u32x4{0, 0, 0, 0});
+        lds_store16(Vbuf + 2 * kTile + 16 * i, u32x4{0, 0, 0, 0});
+    }
+#pragma unroll
+    for (int j = 0; j < NCOPY; ++j) copy_part(0, 0, j);
+    wait_vm_all();
+    __syncthreads();
+    const int n_stage = n_kb + 2;
+    for (int s = 0; s < n_stage; s += 4) {
+        stage(std::integral_constant<int, 0>{}, s);
+        if (s + 1 < n_stage) stage(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 < n_stage) stage(std::integral_constant<int, 2>{}, s + 2);
+        if (s + 3 < n_stage) stage(std::integral_constant<int, 3>{}, s + 3);
     }
     wait_vm_all();
     // The accumulators were last written by matrix products issued from inline
@@ -1928,7 +2037,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
         const long grid = (long)p.B * p.Hq * ((p.N + rows_per_wg - 1) / rows_per_wg);
         const void* fn;
         if constexpr (D <= 128) fn = reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL>);
-        else fn = reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>);
+        else fn = reinterpret_cast<const void*>(&bwd_dq256_kernel<CAUSAL>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, stream);
     }
     return hipSuccess;
