@@ -136,6 +136,20 @@ def extra_figures(torch, fa2, workloads, dev):
             del do, ws, grads
         out[wl.name] = rec
         del q, k, v, o, lse
+    # The headline shape with f16 inputs and outputs (the fa2_*_f16 entry points).
+    wl = workloads.BWD
+    log(f"extra figures: {wl.name} in f16")
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    mk = lambda h: torch.randn(wl.B, h, wl.N, wl.d, device=dev, dtype=torch.float16, generator=g)
+    q, k, v, do = mk(wl.Hq), mk(wl.Hkv), mk(wl.Hkv), mk(wl.Hq)
+    o, lse = fa2.forward(q, k, v, causal=wl.causal)
+    fmed, _ = _median_ms(torch, lambda: fa2.forward(q, k, v, causal=wl.causal, out=o, lse=lse))
+    ws = torch.empty(fa2.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    bmed, _ = _median_ms(torch, lambda: fa2.backward(q, k, v, o, lse, do, causal=wl.causal, workspace=ws,
+                                                     grads=grads), warmup=5, groups=3, per_group=5)
+    out[wl.name + "_f16"] = {"fwd_ms": fmed, "fwd_tflops": wl.fwd_flops() / (fmed * 1e-3) / 1e12,
+                             "bwd_ms": bmed, "bwd_tflops": wl.bwd_flops() / (bmed * 1e-3) / 1e12}
     return out
 
 def main() -> int:

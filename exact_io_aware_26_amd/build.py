@@ -19,6 +19,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip"]
+# Translation units: (source, extra defines, object name).  The kernel sources
+# are compiled twice: for bf16 elements (namespace fa2) and for f16 (fa2_f16).
+UNITS = [("fa2_api.hip", [], "fa2_api"),
+         ("fa2_fwd.hip", [], "fa2_fwd"), ("fa2_bwd.hip", [], "fa2_bwd"),
+         ("fa2_fwd.hip", ["-DFA2_F16=1"], "fa2_fwd_f16"), ("fa2_bwd.hip", ["-DFA2_F16=1"], "fa2_bwd_f16")]
 # Per-source code generation options.  The backward kernels feed matrix-core
 # results straight into vector arithmetic; with this option the compiler keeps
 # those results in ordinary VGPRs instead of accumulation registers that would
@@ -41,9 +46,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa2.so)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit, extra: list[str]) -> str:
+    src, defines, name = unit
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *defines, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is expected.
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
@@ -58,8 +64,8 @@ def build(extra: list[str] | None = None) -> str:
     """Compile all sources in parallel and link libfa2.so; returns its path."""
     extra = list(extra or [])
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
+        objs = list(ex.map(lambda u: _compile(u, extra), UNITS))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -211,8 +211,13 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
     return workspace_layout(rows_pad, q_elems).total;
 }
 
-fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq,
-                   int Hkv, int N, int d, int causal, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward for either element format (f16: the kernels compiled into fa2_f16).
+fa2_status fwd_impl(bool f16, const void* Q, const void* K, const void* V, void* O, float* L, int B,
+                    int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
     g_last_error[0] = '\0';
     bool empty;
     Sizes sz;
@@ -231,23 +236,17 @@ fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* 
     p.G = Hq / Hkv;
     p.n_qtiles = (N + fa2::kFwdRows - 1) / fa2::kFwdRows;
     p.c = (float)((double)scale * kLog2e);
-    hipError_t e = fa2::launch_fwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = f16 ? fa2_f16::launch_fwd(p, d, causal != 0, st) : fa2::launch_fwd(p, d, causal != 0, st);
     if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
     return FA2_OK;
 }
 
-fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
-                   const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                   size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
-                   float scale, void* stream) {
-    return fa2_bwd_stages(FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
-                          B, Hq, Hkv, N, d, causal, scale, stream);
-}
-
-fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const void* V,
-                          const void* O, const float* L, const void* dO, void* dQ, void* dK,
-                          void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
-                          int Hkv, int N, int d, int causal, float scale, void* stream) {
+// The backward stages for either element format.
+fa2_status bwd_impl(bool f16, unsigned stages, const void* Q, const void* K, const void* V,
+                    const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float scale, void* stream) {
     g_last_error[0] = '\0';
     if ((stages & FA2_BWD_ALL) == 0 || (stages & ~(FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC)) != 0)
         return fail(FA2_ERR_INVALID_ARGUMENT,
@@ -279,9 +278,57 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
     p.G = Hq / Hkv;
     p.scale = scale;
     p.c = (float)((double)scale * kLog2e);
-    hipError_t e = fa2::launch_bwd(p, d, causal != 0, stages, static_cast<hipStream_t>(stream));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = f16 ? fa2_f16::launch_bwd(p, d, causal != 0, stages, st)
+                       : fa2::launch_bwd(p, d, causal != 0, stages, st);
     if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
     return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale, void* stream) {
+    return fwd_impl(false, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_fwd_f16(const void* Q, const void* K, const void* V, void* O, float* L, int B,
+                       int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
+    return fwd_impl(true, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                   const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                   size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float scale, void* stream) {
+    return bwd_impl(false, FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
+                    B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const void* V,
+                          const void* O, const float* L, const void* dO, void* dQ, void* dK,
+                          void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
+                          int Hkv, int N, int d, int causal, float scale, void* stream) {
+    return bwd_impl(false, stages, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
+                    Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_f16(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                       const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                       size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                       float scale, void* stream) {
+    return bwd_impl(true, FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
+                    B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_stages_f16(unsigned stages, const void* Q, const void* K, const void* V,
+                              const void* O, const float* L, const void* dO, void* dQ, void* dK,
+                              void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
+                              int Hkv, int N, int d, int causal, float scale, void* stream) {
+    return bwd_impl(true, stages, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
+                    Hkv, N, d, causal, scale, stream);
 }
 
 }  // extern "C"

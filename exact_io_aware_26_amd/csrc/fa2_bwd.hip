@@ -51,7 +51,7 @@
 #include "fa2_device.h"
 #include "fa2_kernels.h"
 
-namespace fa2 {
+namespace FA2_NS {
 
 namespace {
 
@@ -78,7 +78,7 @@ template <int RB> __device__ __forceinline__ int tile_off(int row, int col) {
 // A 32x16 (or 16x32) MFMA operand whose reduction index runs along the rows
 // of a row-major LDS tile: two transposed reads (rows r0.. and r0+8..).
 template <int RB>
-__device__ __forceinline__ bf16x8 tr_operand(const FA2_LDS char* tile, int r0, int c0, int lane) {
+__device__ __forceinline__ el8 tr_operand(const FA2_LDS char* tile, int r0, int c0, int lane) {
     const int j16 = lane & 15;
     const int g = lane >> 5;
     const int row = r0 + 4 * g + (j16 >> 2);
@@ -90,10 +90,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const FA2_LDS char* tile, int r0, i
 
 // A row operand: lane holds row r0 + lane%32, 8 consecutive columns c0 + 8*(lane/32).
 template <int RB>
-__device__ __forceinline__ bf16x8 row_operand(const FA2_LDS char* tile, int r0, int c0, int lane) {
+__device__ __forceinline__ el8 row_operand(const FA2_LDS char* tile, int r0, int c0, int lane) {
     const int row = r0 + (lane & 31);
     const int col = c0 + 8 * (lane >> 5);
-    return as_bf16x8(lds_load16(tile + tile_off<RB>(row, col)));
+    return as_el8(lds_load16(tile + tile_off<RB>(row, col)));
 }
 
 // bwd_main (d = 256 only): BC keys per workgroup (32 per wave), BR query rows
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t x = a[i], y = b[i];
-            acc = fmaf(u32_as_f32(x << 16), u32_as_f32(y << 16), acc);
-            acc = fmaf(u32_as_f32(x & 0xffff0000u), u32_as_f32(y & 0xffff0000u), acc);
+            acc = fmaf(lo_el_f32(x), lo_el_f32(y), acc);
+            acc = fmaf(hi_el_f32(x), hi_el_f32(y), acc);
         }
         if (zero_dq) {
             float* z = p.dQacc + off;
@@ -202,7 +202,7 @@ void bwd_main_kernel(const BwdParams p) {
             if (!KV_REGS) lds_store16(Vs + tile_off<RB_D>(row, col), vx);
         }
     }
-    bf16x8 kf[KV_REGS ? KSD : 1], vf[KV_REGS ? KSD : 1];
+    el8 kf[KV_REGS ? KSD : 1], vf[KV_REGS ? KSD : 1];
     if (KV_REGS) {
 #pragma unroll
         for (int ks = 0; ks < (KV_REGS ? KSD : 1); ++ks) {
@@ -211,8 +211,8 @@ void bwd_main_kernel(const BwdParams p) {
                 kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
                 vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
             }
-            kf[ks] = as_bf16x8(kx);
-            vf[ks] = as_bf16x8(vx);
+            kf[ks] = as_el8(kx);
+            vf[ks] = as_el8(vx);
         }
     }
 
@@ -301,8 +301,8 @@ void bwd_main_kernel(const BwdParams p) {
                 kk_end = min(KSKV, last_q / 16 + 1);
             }
             for (int kk = 0; kk < kk_end; ++kk) {
-                const bf16x8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
-                const bf16x8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
+                const el8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
+                const el8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
                 acc = mfma32(a, bk, acc);
             }
             const int d = 32 * db + li;
@@ -365,9 +365,9 @@ void bwd_main_kernel(const BwdParams p) {
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const bf16x8 aq = row_operand<RB_D>(Qs, 32 * qb, 16 * ks, lane);
-                const bf16x8 ao = row_operand<RB_D>(dOs, 32 * qb, 16 * ks, lane);
-                bf16x8 bk, bv;
+                const el8 aq = row_operand<RB_D>(Qs, 32 * qb, 16 * ks, lane);
+                const el8 ao = row_operand<RB_D>(dOs, 32 * qb, 16 * ks, lane);
+                el8 bk, bv;
                 if (KV_REGS) {
                     bk = kf[KV_REGS ? ks : 0];
                     bv = vf[KV_REGS ? ks : 0];
@@ -399,10 +399,10 @@ void bwd_main_kernel(const BwdParams p) {
                     pr[e] = exp2_fast(fmaf(s[r], p.c, -lv[e]));
                     dsr[e] = pr[e] * (dp[r] - dd[e]);
                 }
-                pp[2 * rq] = pack_bf16(pr[0], pr[1]);
-                pp[2 * rq + 1] = pack_bf16(pr[2], pr[3]);
-                sp[2 * rq] = pack_bf16(dsr[0], dsr[1]);
-                sp[2 * rq + 1] = pack_bf16(dsr[2], dsr[3]);
+                pp[2 * rq] = pack_el(pr[0], pr[1]);
+                pp[2 * rq + 1] = pack_el(pr[2], pr[3]);
+                sp[2 * rq] = pack_el(dsr[0], dsr[1]);
+                sp[2 * rq + 1] = pack_el(dsr[2], dsr[3]);
                 // dS^T[key][query .. query+3]
                 *reinterpret_cast<FA2_LDS u32x2*>(dSt + tile_off<RB_Q>(32 * wave + li, ql)) =
                     u32x2{sp[2 * rq], sp[2 * rq + 1]};
@@ -410,13 +410,13 @@ void bwd_main_kernel(const BwdParams p) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int kk = 2 * qb + h;
-                const bf16x8 bp = as_bf16x8(u32x4{pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]});
-                const bf16x8 bs = as_bf16x8(u32x4{sp[4 * h], sp[4 * h + 1], sp[4 * h + 2], sp[4 * h + 3]});
+                const el8 bp = as_el8(u32x4{pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]});
+                const el8 bs = as_el8(u32x4{sp[4 * h], sp[4 * h + 1], sp[4 * h + 2], sp[4 * h + 3]});
 #pragma unroll
                 for (int db = 0; db < NBD; ++db) {
-                    const bf16x8 ao = tr_operand<RB_D>(dOs, 16 * kk, 32 * db, lane);
+                    const el8 ao = tr_operand<RB_D>(dOs, 16 * kk, 32 * db, lane);
                     dv[db] = mfma32(ao, bp, dv[db]);
-                    const bf16x8 aq = tr_operand<RB_D>(Qs, 16 * kk, 32 * db, lane);
+                    const el8 aq = tr_operand<RB_D>(Qs, 16 * kk, 32 * db, lane);
                     dk[db] = mfma32(aq, bs, dk[db]);
                 }
             }
@@ -436,11 +436,11 @@ void bwd_main_kernel(const BwdParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int d0 = 32 * db + 8 * rq + 4 * g;
                 *reinterpret_cast<u32x2*>(dVr + d0) =
-                    u32x2{pack_bf16(dv[db][4 * rq], dv[db][4 * rq + 1]),
-                          pack_bf16(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
+                    u32x2{pack_el(dv[db][4 * rq], dv[db][4 * rq + 1]),
+                          pack_el(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
                 *reinterpret_cast<u32x2*>(dKr + d0) =
-                    u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
-                          pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+                    u32x2{pack_el(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
+                          pack_el(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
             }
     }
 }
@@ -518,7 +518,7 @@ void bwd_pair_kernel(const BwdParams p) {
             lds_store16(Ks + tile_off<RB_D>(row, col), kx);
         }
     }
-    bf16x8 kf[KSD], vf[KSD];
+    el8 kf[KSD], vf[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
         u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
@@ -526,8 +526,8 @@ void bwd_pair_kernel(const BwdParams p) {
             kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
             vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
         }
-        kf[ks] = as_bf16x8(kx);
-        vf[ks] = as_bf16x8(vx);
+        kf[ks] = as_el8(kx);
+        vf[ks] = as_el8(vx);
     }
     f32x16 dv[NBH], dk[NBH];
 #pragma unroll
@@ -582,8 +582,8 @@ void bwd_pair_kernel(const BwdParams p) {
         int kk_end = KSKV;
         if (CAUSAL) kk_end = min(KSKV, (qt0 + 32 * qb + 31 - kv0) / 16 + 1);
         for (int kk = 0; kk < kk_end; ++kk) {
-            const bf16x8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
-            const bf16x8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
+            const el8 a = tr_operand<RB_Q>(dSt, 16 * kk, 32 * qb, lane);
+            const el8 bk = tr_operand<RB_D>(Ks, 16 * kk, 32 * db, lane);
             acc = mfma32(a, bk, acc);
         }
         // Output row i = 8*(r/4) + 4g + r%4 holds dS^T column i, i.e. query swap23(i).
@@ -646,8 +646,8 @@ void bwd_pair_kernel(const BwdParams p) {
             }
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const bf16x8 aq = row_operand<RB_D>(Qs, 32 * h, 16 * ks, lane);
-                const bf16x8 ao = row_operand<RB_D>(dOs, 32 * h, 16 * ks, lane);
+                const el8 aq = row_operand<RB_D>(Qs, 32 * h, 16 * ks, lane);
+                const el8 ao = row_operand<RB_D>(dOs, 32 * h, 16 * ks, lane);
                 s = mfma32(aq, kf[ks], s);
                 dp = mfma32(ao, vf[ks], dp);
             }
@@ -672,8 +672,8 @@ void bwd_pair_kernel(const BwdParams p) {
                 }
                 const int pos = 32 * h + swap23(8 * rq + 4 * g);   // 4 queries stay contiguous
                 const int off = tile_off<RB_Q>(32 * kvb + li, pos);
-                *reinterpret_cast<FA2_LDS u32x2*>(Pt + off) = u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
-                *reinterpret_cast<FA2_LDS u32x2*>(dSt + off) = u32x2{pack_bf16(dsr[0], dsr[1]), pack_bf16(dsr[2], dsr[3])};
+                *reinterpret_cast<FA2_LDS u32x2*>(Pt + off) = u32x2{pack_el(pr[0], pr[1]), pack_el(pr[2], pr[3])};
+                *reinterpret_cast<FA2_LDS u32x2*>(dSt + off) = u32x2{pack_el(dsr[0], dsr[1]), pack_el(dsr[2], dsr[3])};
             }
         }
         __syncthreads();                         // (X) P^T, dS^T of both query blocks visible
@@ -683,14 +683,14 @@ void bwd_pair_kernel(const BwdParams p) {
         for (int kk = 0; kk < BR / 16; ++kk) {
             const int row = 32 * kvb + li;
             const int col = 16 * kk + 8 * g;
-            const bf16x8 bp = as_bf16x8(lds_load16(Pt + tile_off<RB_Q>(row, col)));
-            const bf16x8 bs = as_bf16x8(lds_load16(dSt + tile_off<RB_Q>(row, col)));
+            const el8 bp = as_el8(lds_load16(Pt + tile_off<RB_Q>(row, col)));
+            const el8 bs = as_el8(lds_load16(dSt + tile_off<RB_Q>(row, col)));
 #pragma unroll
             for (int j = 0; j < NBH; ++j) {
                 const int dcol = (D / 2) * h + 32 * j;
-                const bf16x8 ao = tr_operand<RB_D>(dOs, 16 * kk, dcol, lane);
+                const el8 ao = tr_operand<RB_D>(dOs, 16 * kk, dcol, lane);
                 dv[j] = mfma32(ao, bp, dv[j]);
-                const bf16x8 aq = tr_operand<RB_D>(Qs, 16 * kk, dcol, lane);
+                const el8 aq = tr_operand<RB_D>(Qs, 16 * kk, dcol, lane);
                 dk[j] = mfma32(aq, bs, dk[j]);
             }
         }
@@ -710,11 +710,11 @@ void bwd_pair_kernel(const BwdParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int d0 = (D / 2) * h + 32 * j + 8 * rq + 4 * g;
                 *reinterpret_cast<u32x2*>(dVr + d0) =
-                    u32x2{pack_bf16(dv[j][4 * rq], dv[j][4 * rq + 1]),
-                          pack_bf16(dv[j][4 * rq + 2], dv[j][4 * rq + 3])};
+                    u32x2{pack_el(dv[j][4 * rq], dv[j][4 * rq + 1]),
+                          pack_el(dv[j][4 * rq + 2], dv[j][4 * rq + 3])};
                 *reinterpret_cast<u32x2*>(dKr + d0) =
-                    u32x2{pack_bf16(dk[j][4 * rq] * p.scale, dk[j][4 * rq + 1] * p.scale),
-                          pack_bf16(dk[j][4 * rq + 2] * p.scale, dk[j][4 * rq + 3] * p.scale)};
+                    u32x2{pack_el(dk[j][4 * rq] * p.scale, dk[j][4 * rq + 1] * p.scale),
+                          pack_el(dk[j][4 * rq + 2] * p.scale, dk[j][4 * rq + 3] * p.scale)};
             }
     }
 }
@@ -782,7 +782,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     const int q0 = qtile * BRQ;
     const int wq0 = q0 + 32 * U * wave;
 
-    bf16x8 qf[U][KSD], of[U][KSD];
+    el8 qf[U][KSD], of[U][KSD];
     float l2[U], dq_d[U];
     int qu[U];
 #pragma unroll
@@ -796,8 +796,8 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
                 a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
                 c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
             }
-            qf[u][ks] = as_bf16x8(a);
-            of[u][ks] = as_bf16x8(c);
+            qf[u][ks] = as_el8(a);
+            of[u][ks] = as_el8(c);
         }
         const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
         l2[u] = q < N ? p.L2[row] : kInf;
@@ -863,7 +863,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[1][u][r] = -kInf;
 
-    bf16x8 abuf[kPrefetch];           // operands loaded ahead of their products
+    el8 abuf[kPrefetch];           // operands loaded ahead of their products
     auto stage = [&](auto s8_tag, int s) __attribute__((always_inline)) {
         constexpr int S8 = decltype(s8_tag)::value;
         constexpr int P_SD = S8 & 1;
@@ -871,20 +871,20 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         // Operand load k of stage T8 (mod 8): block T8 lives in tile buffer
         // (T8 >> 1) & 3, block T8 - 2 in the buffer before it; both at rows
         // 32 * (T8 & 1).  Every offset is a compile-time immediate.
-        auto load_at = [&](auto t8_tag, int k) -> bf16x8 {
+        auto load_at = [&](auto t8_tag, int k) -> el8 {
             constexpr int T8 = decltype(t8_tag)::value;
             constexpr int off_sd = ((T8 >> 1) & 3) * kTile + 32 * (T8 & 1) * RB;
             constexpr int off_q = (((T8 >> 1) + 3) & 3) * kTile + 32 * (T8 & 1) * RB;
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
-                return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
+                return as_el8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
             const int off = off_q + 16 * h * RB;
             return cat_tr(lds_load_tr(tp1[db] + off), lds_load_tr(tp2[db] + off));
         };
         auto load_a = [&](int k) { return load_at(s8_tag, k); };
-        auto product = [&](int k, int u, bf16x8 a) {
+        auto product = [&](int k, int u, el8 a) {
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
                 if (j & 1) dpc[P_SD][u] = mfma32(a, of[u][ks], ks == 0 ? zero16() : dpc[P_SD][u]);
@@ -892,13 +892,13 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
                 return;
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
-            const bf16x8 bds = as_bf16x8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
+            const el8 bds = as_el8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
                                                dsp[P_SD][u][4 * h + 2], dsp[P_SD][u][4 * h + 3]});
             // Issued as assembly to keep the accumulator in AGPRs (the compiler
             // places every builtin product's result in VGPRs here, which would
             // not fit); acc[u][db] is next touched a dozen products later.
             f32x16 c = acc[u][db];
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
+            asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
             acc[u][db] = c;
         };
         auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
@@ -921,7 +921,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
             pin(x);
             dpc[P_EL][u][r] = x;
             if (r & 1) {
-                uint32_t w = pack_bf16(dpc[P_EL][u][r - 1], x);
+                uint32_t w = pack_el(dpc[P_EL][u][r - 1], x);
                 pin_u(w);
                 dsp[P_EL][u][r >> 1] = w;
             }
@@ -952,7 +952,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         // 2 * SL product slots: load k feeds slots 2k (u = 0) and 2k + 1 (u = 1).
 #pragma unroll
         for (int k = 0; k < SL; ++k) {
-            const bf16x8 a = abuf[k % kPrefetch];
+            const el8 a = abuf[k % kPrefetch];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -1015,8 +1015,8 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
                 for (int rq = 0; rq < 4; ++rq) {
                     const int d0 = 32 * db + 8 * rq + 4 * g;
                     *reinterpret_cast<u32x2*>(dQr + d0) =
-                        u32x2{pack_bf16(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
-                              pack_bf16(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
+                        u32x2{pack_el(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
+                              pack_el(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
                 }
         }
     }
@@ -1070,7 +1070,7 @@ void bwd_dq256_kernel(const BwdParams p) {
     const int q0 = qtile * BRQ;
     const int wq0 = q0 + 32 * U * wave;
 
-    bf16x8 qf[U][KSD], of[U][KSD];
+    el8 qf[U][KSD], of[U][KSD];
     float l2[U], dq_d[U];
     int qu[U];
 #pragma unroll
@@ -1084,8 +1084,8 @@ void bwd_dq256_kernel(const BwdParams p) {
                 a = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
                 c = global_load16(p.dO + qhead + (size_t)q * D + 16 * ks + 8 * g);
             }
-            qf[u][ks] = as_bf16x8(a);
-            of[u][ks] = as_bf16x8(c);
+            qf[u][ks] = as_el8(a);
+            of[u][ks] = as_el8(c);
         }
         const size_t row = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + min(q, N - 1);
         l2[u] = q < N ? p.L2[row] : kInf;
@@ -1151,7 +1151,7 @@ void bwd_dq256_kernel(const BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[1][u][r] = -kInf;
 
-    bf16x8 abuf[kPrefetch];           // operands loaded ahead of their products
+    el8 abuf[kPrefetch];           // operands loaded ahead of their products
     auto stage = [&](auto s4_tag, int s) __attribute__((always_inline)) {
         constexpr int S4 = decltype(s4_tag)::value;
         constexpr int P_SD = S4 & 1;
@@ -1159,18 +1159,18 @@ void bwd_dq256_kernel(const BwdParams p) {
         // Operand load k of stage S4 (mod 4): block S4 is tile buffer S4, block
         // S4 - 2 the buffer two before it.  Every offset is a compile-time
         // immediate.
-        auto load_a = [&](int k) -> bf16x8 {
+        auto load_a = [&](int k) -> el8 {
             constexpr int off_sd = (S4 & 3) * kTile;
             constexpr int off_q = ((S4 + 2) & 3) * kTile;
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
-                return as_bf16x8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
+                return as_el8(lds_load16(((j & 1) ? vp[ks] : kp[ks]) + off_sd));
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
             const int off = off_q + 16 * h * RB;
             return cat_tr(lds_load_tr(tp1[db] + off), lds_load_tr(tp2[db] + off));
         };
-        auto product = [&](int k, int u, bf16x8 a) {
+        auto product = [&](int k, int u, el8 a) {
             if (k % 3 != 2) {
                 const int j = 2 * (k / 3) + k % 3, ks = j >> 1;
                 if (j & 1) dpc[P_SD][u] = mfma32(a, of[u][ks], ks == 0 ? zero16() : dpc[P_SD][u]);
@@ -1178,13 +1178,13 @@ void bwd_dq256_kernel(const BwdParams p) {
                 return;
             }
             const int qq = k / 3, h = qq / NBD, db = qq % NBD;
-            const bf16x8 bds = as_bf16x8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
+            const el8 bds = as_el8(u32x4{dsp[P_SD][u][4 * h], dsp[P_SD][u][4 * h + 1],
                                                dsp[P_SD][u][4 * h + 2], dsp[P_SD][u][4 * h + 3]});
             // Issued as assembly to keep the accumulator in AGPRs (the compiler
             // places every builtin product's result in VGPRs here, which would
             // not fit); acc[u][db] is next touched a dozen products later.
             f32x16 c = acc[u][db];
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
+            asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bds));
             acc[u][db] = c;
         };
         auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
@@ -1207,7 +1207,7 @@ void bwd_dq256_kernel(const BwdParams p) {
             pin(x);
             dpc[P_EL][u][r] = x;
             if (r & 1) {
-                uint32_t w = pack_bf16(dpc[P_EL][u][r - 1], x);
+                uint32_t w = pack_el(dpc[P_EL][u][r - 1], x);
                 pin_u(w);
                 dsp[P_EL][u][r >> 1] = w;
             }
@@ -1233,7 +1233,7 @@ void bwd_dq256_kernel(const BwdParams p) {
         // 2 * SL product slots: load k feeds slots 2k (u = 0) and 2k + 1 (u = 1).
 #pragma unroll
         for (int k = 0; k < SL; ++k) {
-            const bf16x8 a = abuf[k % kPrefetch];
+            const el8 a = abuf[k % kPrefetch];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -1287,8 +1287,8 @@ void bwd_dq256_kernel(const BwdParams p) {
                 for (int rq = 0; rq < 4; ++rq) {
                     const int d0 = 32 * db + 8 * rq + 4 * g;
                     *reinterpret_cast<u32x2*>(dQr + d0) =
-                        u32x2{pack_bf16(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
-                              pack_bf16(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
+                        u32x2{pack_el(acc[u][db][4 * rq] * p.scale, acc[u][db][4 * rq + 1] * p.scale),
+                              pack_el(acc[u][db][4 * rq + 2] * p.scale, acc[u][db][4 * rq + 3] * p.scale)};
                 }
         }
     }
@@ -1353,7 +1353,7 @@ void bwd_kv_kernel(const BwdParams p) {
     const int kv = kw0 + li;
     const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
 
-    bf16x8 kf[KSD], vf[KSD];
+    el8 kf[KSD], vf[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
         u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
@@ -1361,8 +1361,8 @@ void bwd_kv_kernel(const BwdParams p) {
             kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
             vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
         }
-        kf[ks] = as_bf16x8(kx);
-        vf[ks] = as_bf16x8(vx);
+        kf[ks] = as_el8(kx);
+        vf[ks] = as_el8(vx);
     }
     f32x16 dv[NBD], dk[NBD];
 #pragma unroll
@@ -1472,17 +1472,17 @@ void bwd_kv_kernel(const BwdParams p) {
             for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
         };
         // A operand of product k.
-        auto load_a = [&](int k) -> bf16x8 {
+        auto load_a = [&](int k) -> el8 {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
                 const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
-                return as_bf16x8(lds_load16(at(kb ^ (32 * ks)) + off));
+                return as_el8(lds_load16(at(kb ^ (32 * ks)) + off));
             }
             const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
             const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
             return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
         };
-        auto product = [&](int k, bf16x8 a) {
+        auto product = [&](int k, el8 a) {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
                 if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
@@ -1491,10 +1491,10 @@ void bwd_kv_kernel(const BwdParams p) {
             }
             const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
             if (jj & 1) {
-                const bf16x8 bs = as_bf16x8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
+                const el8 bs = as_el8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
                 dk[db] = mfma32(a, bs, dk[db]);
             } else {
-                const bf16x8 bp = as_bf16x8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
+                const el8 bp = as_el8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
                 dv[db] = mfma32(a, bp, dv[db]);
             }
         };
@@ -1523,7 +1523,7 @@ void bwd_kv_kernel(const BwdParams p) {
             pin(ds);
             dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
             if (r & 1) {
-                uint32_t a = pack_bf16(sc[blk][r - 1], pr), c = pack_bf16(dpc[blk][r - 1], ds);
+                uint32_t a = pack_el(sc[blk][r - 1], pr), c = pack_el(dpc[blk][r - 1], ds);
                 pin_u(a);
                 pin_u(c);
                 pp[blk][r >> 1] = a;
@@ -1567,10 +1567,10 @@ void bwd_kv_kernel(const BwdParams p) {
         // -D of block 0 before the first operands: its dP products start at slot 1.
 #pragma unroll
         for (int rl = 0; rl < 4; ++rl) load_nd(0, rl);
-        bf16x8 abuf[kPrefetch];
+        el8 abuf[kPrefetch];
         auto slot = [&](int k) {
             __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 a = abuf[k % kPrefetch];
+            const el8 a = abuf[k % kPrefetch];
             if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
             product(k, a);
             vector_work(k);
@@ -1623,11 +1623,11 @@ void bwd_kv_kernel(const BwdParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int d0 = 32 * db + 8 * rq + 4 * g;
                 *reinterpret_cast<u32x2*>(dVr + d0) =
-                    u32x2{pack_bf16(dv[db][4 * rq], dv[db][4 * rq + 1]),
-                          pack_bf16(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
+                    u32x2{pack_el(dv[db][4 * rq], dv[db][4 * rq + 1]),
+                          pack_el(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
                 *reinterpret_cast<u32x2*>(dKr + d0) =
-                    u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
-                          pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+                    u32x2{pack_el(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
+                          pack_el(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
             }
     }
 }
@@ -1683,7 +1683,7 @@ void bwd_kv256_kernel(const BwdParams p) {
     const int kv = kw0 + li;
     const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
 
-    bf16x8 kf[KSD], vf[KSD];
+    el8 kf[KSD], vf[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
         u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
@@ -1691,8 +1691,8 @@ void bwd_kv256_kernel(const BwdParams p) {
             kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
             vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
         }
-        kf[ks] = as_bf16x8(kx);
-        vf[ks] = as_bf16x8(vx);
+        kf[ks] = as_el8(kx);
+        vf[ks] = as_el8(vx);
     }
     f32x16 dv[NBD], dk[NBD];
 #pragma unroll
@@ -1804,17 +1804,17 @@ void bwd_kv256_kernel(const BwdParams p) {
             for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
         };
         // A operand of product k.
-        auto load_a = [&](int k) -> bf16x8 {
+        auto load_a = [&](int k) -> el8 {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
                 const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
-                return as_bf16x8(lds_load16(at(kb ^ (32 * ks)) + off));
+                return as_el8(lds_load16(at(kb ^ (32 * ks)) + off));
             }
             const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
             const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
             return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
         };
-        auto product = [&](int k, bf16x8 a) {
+        auto product = [&](int k, el8 a) {
             if (k < 2 * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
                 if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
@@ -1825,14 +1825,14 @@ void bwd_kv256_kernel(const BwdParams p) {
             // Issued as assembly to keep the accumulators in AGPRs (with the
             // whole head dim of K and V as operands they do not fit in VGPRs).
             if (jj & 1) {
-                const bf16x8 bs = as_bf16x8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
+                const el8 bs = as_el8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
                 f32x16 c = dk[db];
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bs));
+                asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bs));
                 dk[db] = c;
             } else {
-                const bf16x8 bp = as_bf16x8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
+                const el8 bp = as_el8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
                 f32x16 c = dv[db];
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bp));
+                asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bp));
                 dv[db] = c;
             }
         };
@@ -1861,7 +1861,7 @@ void bwd_kv256_kernel(const BwdParams p) {
             pin(ds);
             dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
             if (r & 1) {
-                uint32_t a = pack_bf16(sc[blk][r - 1], pr), c = pack_bf16(dpc[blk][r - 1], ds);
+                uint32_t a = pack_el(sc[blk][r - 1], pr), c = pack_el(dpc[blk][r - 1], ds);
                 pin_u(a);
                 pin_u(c);
                 pp[blk][r >> 1] = a;
@@ -1904,10 +1904,10 @@ void bwd_kv256_kernel(const BwdParams p) {
         // -D of block 0 before the first operands: its dP products start at slot 1.
 #pragma unroll
         for (int rl = 0; rl < 4; ++rl) load_nd(0, rl);
-        bf16x8 abuf[kPrefetch];
+        el8 abuf[kPrefetch];
         auto slot = [&](int k) {
             __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 a = abuf[k % kPrefetch];
+            const el8 a = abuf[k % kPrefetch];
             if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
             product(k, a);
             vector_work(k);
@@ -1958,11 +1958,11 @@ void bwd_kv256_kernel(const BwdParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int d0 = DH * half + 32 * db + 8 * rq + 4 * g;
                 *reinterpret_cast<u32x2*>(dVr + d0) =
-                    u32x2{pack_bf16(dv[db][4 * rq], dv[db][4 * rq + 1]),
-                          pack_bf16(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
+                    u32x2{pack_el(dv[db][4 * rq], dv[db][4 * rq + 1]),
+                          pack_el(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
                 *reinterpret_cast<u32x2*>(dKr + d0) =
-                    u32x2{pack_bf16(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
-                          pack_bf16(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
+                    u32x2{pack_el(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
+                          pack_el(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
             }
     }
 }
@@ -1976,10 +1976,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const BwdParams p, 
     const u32x4 a = *reinterpret_cast<const u32x4*>(src);
     const u32x4 c = *reinterpret_cast<const u32x4*>(src + 4);
     u32x4 out;
-    out[0] = pack_bf16(u32_as_f32(a[0]) * p.scale, u32_as_f32(a[1]) * p.scale);
-    out[1] = pack_bf16(u32_as_f32(a[2]) * p.scale, u32_as_f32(a[3]) * p.scale);
-    out[2] = pack_bf16(u32_as_f32(c[0]) * p.scale, u32_as_f32(c[1]) * p.scale);
-    out[3] = pack_bf16(u32_as_f32(c[2]) * p.scale, u32_as_f32(c[3]) * p.scale);
+    out[0] = pack_el(u32_as_f32(a[0]) * p.scale, u32_as_f32(a[1]) * p.scale);
+    out[1] = pack_el(u32_as_f32(a[2]) * p.scale, u32_as_f32(a[3]) * p.scale);
+    out[2] = pack_el(u32_as_f32(c[0]) * p.scale, u32_as_f32(c[1]) * p.scale);
+    out[3] = pack_el(u32_as_f32(c[2]) * p.scale, u32_as_f32(c[3]) * p.scale);
     *reinterpret_cast<u32x4*>(p.dQ + i * 8) = out;
 }
 
@@ -2054,4 +2054,4 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, h
     }
 }
 
-}  // namespace fa2
+}  // namespace FA2_NS

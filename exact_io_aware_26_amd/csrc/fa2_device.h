@@ -10,14 +10,34 @@
 //     (i = 8*(r/4) + 4*g + r%4, j = l % 32).
 // The reduction elements a lane holds only have to agree between A and B,
 // so every kernel here picks the reduction order that suits its operands.
+//
+// Element format.  Q, K, V, O, dO and the gradients are bf16 by default; the
+// kernel sources compiled with FA2_F16=1 take and produce f16 instead (the same
+// kernels: operands are 16-bit patterns moved through registers and LDS, and
+// only the matrix-product instruction, the fp32 -> 16-bit packing and the
+// 16-bit -> fp32 reads below depend on the format).  The two builds live in
+// namespaces fa2 and fa2_f16.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace fa2 {
+#ifndef FA2_F16
+#define FA2_F16 0
+#endif
+#if FA2_F16
+#define FA2_NS fa2_f16
+#define FA2_MFMA_32X32X16 "v_mfma_f32_32x32x16_f16"
+#else
+#define FA2_NS fa2
+#define FA2_MFMA_32X32X16 "v_mfma_f32_32x32x16_bf16"
+#endif
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+namespace FA2_NS {
+
+typedef __bf16 el8 __attribute__((ext_vector_type(8)));      // 8 elements: MFMA operand storage
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -33,8 +53,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float u32_as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ uint32_t f32_as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma32(el8 a, el8 b, f32x16 c) {
+#if FA2_F16
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+#else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -44,13 +69,34 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+// Two fp32 -> two packed elements, rounded to nearest even (bf16:
+// v_cvt_pk_bf16_f32; f16: v_cvt_f16_f32 per value).
+__device__ __forceinline__ uint32_t pack_el(float lo, float hi) {
+#if FA2_F16
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+#else
     bf16x2 v = {(__bf16)lo, (__bf16)hi};
+#endif
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// The element in bits 0..15 / 16..31 of a packed pair, as fp32 (exact).
+__device__ __forceinline__ float lo_el_f32(uint32_t x) {
+#if FA2_F16
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+#else
+    return __builtin_bit_cast(float, x << 16);
+#endif
+}
+__device__ __forceinline__ float hi_el_f32(uint32_t x) {
+#if FA2_F16
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+#else
+    return __builtin_bit_cast(float, x & 0xffff0000u);
+#endif
+}
+
+__device__ __forceinline__ el8 as_el8(u32x4 v) { return __builtin_bit_cast(el8, v); }
 
 // lo + hi of a packed bf16 pair added into an fp32 accumulator (v_dot2c_f32_bf16 with ones).
 __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
@@ -110,10 +156,10 @@ __device__ __forceinline__ s16x4 lds_load_tr(const FA2_LDS char* p) {
         reinterpret_cast<FA2_LDS s16x4*>(const_cast<FA2_LDS char*>(p)));
 }
 
-__device__ __forceinline__ bf16x8 cat_tr(s16x4 a, s16x4 b) {
+__device__ __forceinline__ el8 cat_tr(s16x4 a, s16x4 b) {
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return __builtin_bit_cast(bf16x8, v);
+    return __builtin_bit_cast(el8, v);
 }
 
 // Asynchronous copies from global memory into LDS (global_load_lds_*): lane i
@@ -159,4 +205,4 @@ __device__ __forceinline__ u32x4 global_load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-}  // namespace fa2
+}  // namespace FA2_NS

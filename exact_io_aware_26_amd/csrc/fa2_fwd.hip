@@ -40,7 +40,7 @@
 #include "fa2_device.h"
 #include "fa2_kernels.h"
 
-namespace fa2 {
+namespace FA2_NS {
 
 namespace {
 
@@ -142,12 +142,12 @@ void fwd_kernel(const FwdParams p) {
     const bool wave_live = wq0 < N;
 
     // ---- this lane's query row, as 8-element MFMA operands over the head dim
-    bf16x8 qf[KSD];
+    el8 qf[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
         u32x4 v = {0, 0, 0, 0};
         if (q < N) v = global_load16(Qh + (size_t)q * D + 16 * ks + 8 * g);
-        qf[ks] = as_bf16x8(v);
+        qf[ks] = as_el8(v);
     }
 
     // ---- key tiles this workgroup visits
@@ -188,7 +188,7 @@ void fwd_kernel(const FwdParams p) {
                     const int row = 32 * bs + li;
                     const int chunk = 2 * ks + g;
                     const u32x4 a = lds_load16(Ks + row * (2 * D) + 16 * (chunk ^ swz_k<D>(row)));
-                    s[bs] = mfma32(as_bf16x8(a), qf[ks], s[bs]);
+                    s[bs] = mfma32(as_el8(a), qf[ks], s[bs]);
                 }
             }
 
@@ -223,7 +223,7 @@ void fwd_kernel(const FwdParams p) {
                 for (int r = 0; r < 16; r += 2) {
                     const float p0 = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
                     const float p1 = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
-                    pp[bs][r >> 1] = pack_bf16(p0, p1);
+                    pp[bs][r >> 1] = pack_el(p0, p1);
                     lsum += p0 + p1;
                 }
             l_run = fmaf(l_run, alpha, lsum);
@@ -244,7 +244,7 @@ void fwd_kernel(const FwdParams p) {
                 const int bs = kk >> 1, h = kk & 1;
                 const u32x4 pv = {pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2],
                                   pp[bs][4 * h + 3]};
-                const bf16x8 bfrag = as_bf16x8(pv);
+                const el8 bfrag = as_el8(pv);
                 const int row1 = 16 * kk + 4 * g + (j16 >> 2);
                 const int row2 = row1 + 8;
 #pragma unroll
@@ -277,8 +277,8 @@ void fwd_kernel(const FwdParams p) {
                 for (int rq = 0; rq < 4; ++rq) {
                     const int d0 = 32 * db + 8 * rq + 4 * g;
                     u32x2 w;
-                    w[0] = pack_bf16(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-                    w[1] = pack_bf16(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + d0) = w;
                 }
             if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
@@ -351,12 +351,12 @@ void fwd_pipe_kernel(const FwdParams p) {
     const int wq0 = q0 + 32 * wave;
     const int q = wq0 + li;
 
-    bf16x8 qf[KSD];
+    el8 qf[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
         u32x4 v = {0, 0, 0, 0};
         if (q < N) v = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
-        qf[ks] = as_bf16x8(v);
+        qf[ks] = as_el8(v);
     }
 
     // Tiles the workgroup streams, and tiles this wave computes on.
@@ -410,7 +410,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
             for (int bs = 0; bs < 2; ++bs) {
                 const u32x4 a = lds_load16(Ks + 32 * bs * RB + (kb ^ (32 * ks)));
-                s[bs] = mfma32(as_bf16x8(a), qf[ks], s[bs]);
+                s[bs] = mfma32(as_el8(a), qf[ks], s[bs]);
             }
     };
 
@@ -451,7 +451,7 @@ void fwd_pipe_kernel(const FwdParams p) {
             for (int r = 0; r < 16; r += 2) {
                 s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
                 s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
-                pp[bs][r >> 1] = pack_bf16(s[bs][r], s[bs][r + 1]);
+                pp[bs][r >> 1] = pack_el(s[bs][r], s[bs][r + 1]);
             }
         return alpha;
     };
@@ -477,7 +477,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int bs = kk >> 1, h = kk & 1;
-            const bf16x8 bfrag = as_bf16x8(u32x4{pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2], pp[bs][4 * h + 3]});
+            const el8 bfrag = as_el8(u32x4{pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2], pp[bs][4 * h + 3]});
 #pragma unroll
             for (int db = 0; db < NBD; ++db) {
                 const s16x4 t1 = lds_load_tr(Vs + 16 * kk * RB + (vb1 ^ (64 * db)));
@@ -566,8 +566,8 @@ void fwd_pipe_kernel(const FwdParams p) {
                 for (int rq = 0; rq < 4; ++rq) {
                     const int d0 = 32 * db + 8 * rq + 4 * g;
                     u32x2 w;
-                    w[0] = pack_bf16(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-                    w[1] = pack_bf16(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + d0) = w;
                 }
             if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
@@ -603,4 +603,4 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream
     }
 }
 
-}  // namespace fa2
+}  // namespace FA2_NS

@@ -6,7 +6,7 @@
 namespace fa2 {
 
 struct FwdParams {
-    const uint16_t* Q;  // bf16 [B, Hq, N, D]
+    const uint16_t* Q;  // bf16 (f16 in fa2_f16) [B, Hq, N, D]
     const uint16_t* K;  // bf16 [B, Hkv, N, D]
     const uint16_t* V;  // bf16 [B, Hkv, N, D]
     uint16_t* O;        // bf16 [B, Hq, N, D]
@@ -49,3 +49,14 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream);
 
 }  // namespace fa2
+
+// The same kernels compiled for f16 elements (the kernel sources built with
+// FA2_F16=1); the parameter blocks are shared, their 16-bit pointers then hold f16.
+namespace fa2_f16 {
+using fa2::BwdParams;
+using fa2::FwdParams;
+using fa2::kBwdRowPad;
+using fa2::kFwdRows;
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream);
+}  // namespace fa2_f16

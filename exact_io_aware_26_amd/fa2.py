@@ -22,8 +22,10 @@ FA2_ERR_INVALID_ARGUMENT = 1
 FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
-EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_bwd_workspace_bytes",
-           "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string", "fa2_last_error")
+EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
+           "fa2_bwd_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
+           "fa2_last_error")
+DTYPES = (torch.bfloat16, torch.float16)
 
 BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
 
@@ -53,6 +55,11 @@ def load(path: str | None = None):
     lib.fa2_bwd.restype = i
     lib.fa2_bwd_stages.argtypes = [ctypes.c_uint] + lib.fa2_bwd.argtypes
     lib.fa2_bwd_stages.restype = i
+    for name, like in (("fa2_fwd_f16", lib.fa2_fwd), ("fa2_bwd_f16", lib.fa2_bwd),
+                       ("fa2_bwd_stages_f16", lib.fa2_bwd_stages)):
+        fn = getattr(lib, name)
+        fn.argtypes = like.argtypes
+        fn.restype = i
     lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_bwd_workspace_bytes.restype = sz
     lib.fa2_validate_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
@@ -86,9 +93,11 @@ def _stream_handle(t: torch.Tensor) -> int:
 
 
 def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    if q.dtype not in DTYPES:
+        raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
         if not t.is_contiguous():
@@ -106,8 +115,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
             lse: torch.Tensor | None = None):
     """O = softmax(scale * q k^T [+ causal mask]) v and L (natural-log logsumexp per row).
 
-    q [B,Hq,N,d], k/v [B,Hkv,N,d] contiguous bf16 GPU tensors.  Returns
-    (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32).  scale defaults to 1/sqrt(d).
+    q [B,Hq,N,d], k/v [B,Hkv,N,d] contiguous GPU tensors, all bf16 or all f16.
+    Returns (o [B,Hq,N,d] in q's dtype, lse [B,Hq,N] fp32).  scale defaults to
+    1/sqrt(d).
     """
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
@@ -117,8 +127,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = lib.fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
-                     int(bool(causal)), float(scale), _stream_handle(q))
+    if out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype")
+    fwd = lib.fa2_fwd_f16 if q.dtype == torch.float16 else lib.fa2_fwd
+    st = fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+             int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return out, lse
 
@@ -133,7 +146,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              grads=None, stages: int = BWD_ALL):
     """dQ, dK, dV of sum(do * o) for the forward above (P rebuilt from lse).
 
-    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) bf16.  A caller
+    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) in q's dtype.  A caller
     may pass a reusable uint8 ``workspace`` of at least
     ``workspace_bytes(...)`` bytes (256-byte aligned), preallocated output
     tensors ``grads=(dq, dk, dv)``, and a subset of the launch ``stages``
@@ -142,8 +155,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
     for name, t in (("o", o), ("do", do)):
-        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like q")
+        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped like q, in q's dtype")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
     if scale is None:
@@ -156,12 +169,13 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     else:
         dq, dk, dv = grads
         for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-            if t.dtype != torch.bfloat16 or t.shape != like.shape or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like its input")
+            if t.dtype != q.dtype or t.shape != like.shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor shaped like its input, in q's dtype")
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
-    st = lib.fa2_bwd_stages(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    bwd = lib.fa2_bwd_stages_f16 if q.dtype == torch.float16 else lib.fa2_bwd_stages
+    st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv

@@ -1,13 +1,14 @@
 """Seeded synthetic inputs shared by the tests, the benchmark and the oracle side.
 
 This module holds no attention arithmetic: it draws numbers and rounds them
-to bfloat16.  Both the HIP path and the CPU oracle receive exactly the arrays
+to bfloat16 (or, for the f16 entry points, to IEEE binary16).  Both the HIP path and the CPU oracle receive exactly the arrays
 it returns (the oracle as their exact float64 values).
 
 Recipe: NumPy PCG64 ``default_rng(seed)``, ``standard_normal(shape,
 dtype=float32)`` drawn in the order the caller lists the tensors (Q, K, V,
 then dO), each rounded to bfloat16 with round-to-nearest-even on the upper 16
-bits.  N(0, 1) values never round to NaN or Inf.
+bits (f16: NumPy's float32 -> float16 conversion, also round-to-nearest-even).
+N(0, 1) values never round to NaN or Inf.
 """
 from __future__ import annotations
 
@@ -46,10 +47,27 @@ def seeded_bf16(seed: int, shapes) -> list[np.ndarray]:
     return out
 
 
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE binary16 bit patterns (uint16) to float64."""
+    return np.ascontiguousarray(np.asarray(b, dtype=np.uint16)).view(np.float16).astype(np.float64)
+
+
+def seeded_f16(seed: int, shapes) -> list[np.ndarray]:
+    """The same draws as ``seeded_bf16``, rounded to binary16 bits instead."""
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(tuple(shape), dtype=np.float32).astype(np.float16).view(np.uint16)
+            for shape in shapes]
+
+
 def attention_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int,
-                     with_grad: bool = False) -> list[np.ndarray]:
-    """bf16 bit arrays Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO [B,Hq,N,d])."""
+                     with_grad: bool = False, fmt: str = "bf16") -> list[np.ndarray]:
+    """Bit arrays (uint16) Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO [B,Hq,N,d]),
+    in bf16 (``fmt="bf16"``) or binary16 (``fmt="f16"``)."""
     shapes = [(B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)]
     if with_grad:
         shapes.append((B, Hq, N, d))
+    if fmt == "f16":
+        return seeded_f16(seed, shapes)
+    if fmt != "bf16":
+        raise ValueError(f"unknown element format {fmt!r}")
     return seeded_bf16(seed, shapes)

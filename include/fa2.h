@@ -149,6 +149,26 @@ fa2_status fa2_bwd_stages(unsigned stages, const void *Q, const void *K, const v
                           int Hkv, int N, int d, int causal, float scale, void *stream);
 
 /*
+ * FP16 inputs and outputs (the pages' problem statement allows FP16 or BF16).
+ * Same arguments, layouts, workspace, checks, errors and determinism as
+ * fa2_fwd / fa2_bwd / fa2_bwd_stages, with Q, K, V, O, dO, dQ, dK and dV
+ * holding IEEE binary16 values (L stays fp32).  The same kernels run with f16
+ * matrix products, fp32 accumulation and round-to-nearest-even f16 outputs.
+ */
+fa2_status fa2_fwd_f16(const void *Q, const void *K, const void *V, void *O, float *L,
+                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       void *stream);
+fa2_status fa2_bwd_f16(const void *Q, const void *K, const void *V, const void *O,
+                       const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                       void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                       int N, int d, int causal, float scale, void *stream);
+fa2_status fa2_bwd_stages_f16(unsigned stages, const void *Q, const void *K, const void *V,
+                              const void *O, const float *L, const void *dO, void *dQ,
+                              void *dK, void *dV, void *workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              void *stream);
+
+/*
  * The argument checks of fa2_fwd / fa2_bwd alone: no HIP call is made, so
  * they run without a GPU.  Same return codes as the full calls.
  */

@@ -1,0 +1,114 @@
+"""FP16 inputs and outputs (fa2_fwd_f16 / fa2_bwd_f16) against the fp64 oracle.
+
+The same seeded N(0,1) draws as the bf16 tests, rounded to binary16; the oracle
+receives their exact values.  Outputs are pre-filled with NaN (and the
+workspace with garbage) so that an unwritten element fails.  The gates are the
+ones of the bf16 results (max-abs 1e-2 beyond the rounding of the exact value,
+relative L2 5e-3; L max-abs 1e-3): binary16 has three more mantissa bits than
+bf16, so they hold with room to spare.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from exact_io_aware_26_amd import inputs
+from oracle import oracle as orc
+from tests import parity
+from tests.parity import log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_io_aware_26_amd import fa2
+    fa2.load()
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to("cuda")
+
+
+def to_f64(t):
+    assert t.dtype == torch.float16
+    return inputs.f16_bits_to_f64(t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def fwd_case(seed, B, Hq, Hkv, N, d, causal):
+    from exact_io_aware_26_amd import fa2
+    log(f"[fwd f16] seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    qb, kb, vb = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, fmt="f16")
+    q, k, v = (to_dev(x) for x in (qb, kb, vb))
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    o, L = fa2.forward(q, k, v, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    q64, k64, v64 = (inputs.f16_bits_to_f64(x) for x in (qb, kb, vb))
+    ro, rL = orc.forward(q64, k64, v64, causal, 1.0 / math.sqrt(d))
+    parity.check_bf16("O (f16)", to_f64(o), ro)
+    parity.check_lse("L (f16 inputs)", parity.f32_to_f64(L), rL)
+
+
+def bwd_case(seed, B, Hq, Hkv, N, d, causal, atomic=False):
+    from exact_io_aware_26_amd import fa2
+    log(f"[bwd f16] seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} atomic_dq={atomic}")
+    qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True, fmt="f16")
+    q, k, v, do = (to_dev(x) for x in (qb, kb, vb, dob))
+    o, L = fa2.forward(q, k, v, causal=causal)
+    nbytes = fa2.workspace_bytes(B, Hq, Hkv, N, d)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=q.device)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
+    dq, dk, dv = fa2.backward(q, k, v, o, L, do, causal=causal, workspace=ws, grads=grads, stages=stages)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (inputs.f16_bits_to_f64(x) for x in (qb, kb, vb, dob))
+    rdq, rdk, rdv, _ = orc.backward(q64, k64, v64, do64, causal, 1.0 / math.sqrt(d))
+    parity.check_bf16("dQ (f16)", to_f64(dq), rdq)
+    parity.check_bf16("dK (f16)", to_f64(dk), rdk)
+    parity.check_bf16("dV (f16)", to_f64(dv), rdv)
+
+
+FWD = []
+for N in (1, 65, 130, 257, 1000):
+    for d in (64, 128, 256):
+        for causal in (False, True):
+            heads = [(1, 1), (4, 1), (4, 2), (2, 2)][(N + d // 64 + causal) % 4]
+            FWD.append((1 + N % 2, heads[0], heads[1], N, d, causal))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", FWD)
+def test_f16_forward(B, Hq, Hkv, N, d, causal):
+    fwd_case(700 + N + d, B, Hq, Hkv, N, d, causal)
+
+
+BWD = []
+for N in (17, 130, 257, 1000):
+    for d in (64, 128, 256):
+        for causal in (False, True):
+            heads = [(1, 1), (4, 1), (4, 2), (2, 2)][(N + d // 64 + causal) % 4]
+            BWD.append((1 + N % 2, heads[0], heads[1], N, d, causal))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", BWD)
+def test_f16_backward(B, Hq, Hkv, N, d, causal):
+    bwd_case(800 + N + d, B, Hq, Hkv, N, d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_f16_backward_atomic_mode(d):
+    bwd_case(900 + d, 1, 4, 2, 300, d, True, atomic=True)
+
+
+def test_mixed_element_formats_are_rejected():
+    from exact_io_aware_26_amd import fa2
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16, device="cuda")
+    kb = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError):
+        fa2.forward(q, kb, kb)
+    with pytest.raises(TypeError):
+        fa2.forward(q.float(), q.float(), q.float())

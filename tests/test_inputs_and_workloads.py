@@ -45,3 +45,19 @@ def test_flop_accounting_matches_golden():
         assert workloads.BY_NAME[name].fwd_flops() == want, name
     for name, want in g["bwd"].items():
         assert workloads.BY_NAME[name].bwd_flops() == want, name
+
+
+def test_f16_inputs_are_the_same_draws_rounded_to_binary16():
+    a16 = inputs.attention_inputs(5, 1, 2, 1, 8, 4, with_grad=True, fmt="f16")
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 2, 8, 4), dtype=np.float32)
+    # round to nearest even, as torch's float32 -> float16 conversion does
+    want = torch.from_numpy(q).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(a16[0], want)
+    assert np.array_equal(inputs.f16_bits_to_f64(a16[0]), q.astype(np.float16).astype(np.float64))
+    try:
+        inputs.attention_inputs(5, 1, 1, 1, 4, 4, fmt="fp8")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("an unknown element format must be rejected")
