@@ -24,11 +24,13 @@ SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip"]
 UNITS = [("fa2_api.hip", [], "fa2_api"),
          ("fa2_fwd.hip", [], "fa2_fwd"), ("fa2_bwd.hip", [], "fa2_bwd"),
          ("fa2_fwd.hip", ["-DFA2_F16=1"], "fa2_fwd_f16"), ("fa2_bwd.hip", ["-DFA2_F16=1"], "fa2_bwd_f16")]
-# Per-source code generation options.  The backward kernels feed matrix-core
-# results straight into vector arithmetic; with this option the compiler keeps
-# those results in ordinary VGPRs instead of accumulation registers that would
-# have to be copied out first.
-SOURCE_FLAGS = {"fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"]}
+# Per-source code generation options.  The kernels feed matrix-core results
+# straight into vector arithmetic; with this option the compiler keeps those
+# results in ordinary VGPRs instead of accumulation registers that would have
+# to be copied out first (the d = 64 / 128 forward kernels compile to the same
+# code either way).
+SOURCE_FLAGS = {"fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"],
+                "fa2_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 FLAGS = [

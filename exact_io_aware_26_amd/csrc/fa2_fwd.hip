@@ -12,7 +12,8 @@
 // lie wholly above the diagonal are skipped and only tiles that straddle it
 // (or the ragged end of the sequence) are masked.
 //
-// gfx950 mapping (one workgroup = 4 wave64s = 128 query rows):
+// gfx950 mapping (each wave64 owns 32 query rows; the kernels below give the
+// workgroup shapes, tile sizes and the LDS pipeline):
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: the B operand is the wave's 32 query rows
 //     (kept in VGPRs for the whole loop) and the A operand is K read from
@@ -29,9 +30,7 @@
 //     one FMA per score before v_exp_f32; the row sum is taken from the fp32
 //     probabilities (before their rounding to bf16 for the PV product), so L
 //     stays accurate to fp32 even for rows with few keys.
-//   * K/V tiles are double-buffered in LDS: the next tile's global loads are
-//     in flight while the current tile is computed; one barrier per tile.
-//     LDS rows are XOR-swizzled by 16-byte chunk (no padding) so that the
+//   * LDS rows are XOR-swizzled by 16-byte chunk (no padding) so that the
 //     MFMA operand reads are free of bank conflicts.
 //   * Grid order: the causal query tiles with the most work run first, and
 //     consecutive workgroup ids walk the heads of one query-tile level, so
@@ -44,10 +43,6 @@ namespace FA2_NS {
 
 namespace {
 
-template <int D> struct FwdTile;   // fwd_kernel (d = 256 only)
-template <> struct FwdTile<256> { static constexpr int BC = 32; };
-
-constexpr int kThreads = 256;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -58,232 +53,6 @@ constexpr float kLn2 = 0.693147180559945309f;
 // reads); this pattern puts both on 64 distinct banks.
 template <int D> __device__ __forceinline__ int swz(int row) {
     return D == 64 ? 4 * ((row >> 1) & 1) + ((row >> 2) & 3) : 4 * (row & 3) + ((row >> 2) & 3);
-}
-template <int D> __device__ __forceinline__ int swz_k(int row) { return swz<D>(row); }
-template <int D> __device__ __forceinline__ int swz_v(int row) { return swz<D>(row); }
-
-template <int D, int BC>
-struct TileLoader {
-    static constexpr int kChunksPerRow = D / 8;                 // 16-byte chunks
-    static constexpr int kPerThread = BC * D / 8 / kThreads;    // chunks per thread per tensor
-    static_assert(kPerThread >= 1 && BC * D / 8 % kThreads == 0, "tile/threads mismatch");
-    u32x4 k[kPerThread];
-    u32x4 v[kPerThread];
-
-    __device__ __forceinline__ void load(const uint16_t* Kh, const uint16_t* Vh, int kv0, int N,
-                                         int tid) {
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / kChunksPerRow;
-            const int col = c % kChunksPerRow;
-            const int gr = kv0 + row;
-            if (gr < N) {
-                const size_t off = (size_t)gr * D + col * 8;
-                k[i] = global_load16(Kh + off);
-                v[i] = global_load16(Vh + off);
-            } else {
-                k[i] = u32x4{0, 0, 0, 0};
-                v[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(FA2_LDS char* Ks, FA2_LDS char* Vs, int tid) const {
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / kChunksPerRow;
-            const int col = c % kChunksPerRow;
-            lds_store16(Ks + row * (2 * D) + 16 * (col ^ swz_k<D>(row)), k[i]);
-            lds_store16(Vs + row * (2 * D) + 16 * (col ^ swz_v<D>(row)), v[i]);
-        }
-    }
-};
-
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
-void fwd_kernel(const FwdParams p) {
-    constexpr int BC = FwdTile<D>::BC;
-    constexpr int NBS = BC / 32;        // 32-key blocks of S^T per tile
-    constexpr int KSD = D / 16;         // MFMA reduction steps over the head dim
-    constexpr int NBD = D / 32;         // 32-wide blocks of the head dim (O^T)
-    constexpr int KSKV = BC / 16;       // MFMA reduction steps over the keys of a tile
-    constexpr int kTileBytes = BC * D * 2;
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kTileBytes];
-    FA2_LDS char* smem = (FA2_LDS char*)smem_raw;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int g = lane >> 5;     // lane group: which 8 reduction elements this lane holds
-    const int li = lane & 31;    // query row within the wave's 32
-
-    // ---- work item: heaviest causal query tiles first, heads of a level consecutive
-    const int BH = p.B * p.Hq;
-    const int level = blockIdx.x / BH;
-    const int bh = blockIdx.x - level * BH;
-    const int qtile = p.n_qtiles - 1 - level;
-    int b, hq;
-    level_head(bh, p.Hq, p.G, p.B, b, hq);
-    const int hk = hq / p.G;
-    const int N = p.N;
-
-    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
-    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
-    const uint16_t* Qh = p.Q + qhead;
-    const uint16_t* Kh = p.K + khead;
-    const uint16_t* Vh = p.V + khead;
-
-    const int q0 = qtile * kFwdRows;
-    const int wq0 = q0 + wave * 32;
-    const int q = wq0 + li;
-    const bool wave_live = wq0 < N;
-
-    // ---- this lane's query row, as 8-element MFMA operands over the head dim
-    el8 qf[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        u32x4 v = {0, 0, 0, 0};
-        if (q < N) v = global_load16(Qh + (size_t)q * D + 16 * ks + 8 * g);
-        qf[ks] = as_el8(v);
-    }
-
-    // ---- key tiles this workgroup visits
-    int n_kv = (N + BC - 1) / BC;
-    if (CAUSAL) {
-        const int last = min(q0 + kFwdRows, N) - 1;
-        n_kv = last / BC + 1;
-    }
-
-    f32x16 o[NBD];
-#pragma unroll
-    for (int i = 0; i < NBD; ++i) o[i] = zero16();
-    float m_run = kNegInf;   // running max of c * S (log2 domain), same in lanes l and l^32
-    float l_run = 0.f;       // this lane's part of the running row sum
-
-    TileLoader<D, BC> ld;
-    ld.load(Kh, Vh, 0, N, tid);
-    ld.store(smem, smem + kTileBytes, tid);
-    __syncthreads();
-
-    for (int j = 0; j < n_kv; ++j) {
-        const int kv0 = j * BC;
-        FA2_LDS char* Ks = smem + (j & 1) * (2 * kTileBytes);
-        FA2_LDS char* Vs = Ks + kTileBytes;
-        const bool has_next = j + 1 < n_kv;
-        if (has_next) ld.load(Kh, Vh, kv0 + BC, N, tid);
-
-        const bool active = wave_live && !(CAUSAL && kv0 > wq0 + 31);
-        if (active) {
-            // S^T = K Q^T for this tile: NBS blocks of 32 keys x 32 query rows.
-            f32x16 s[NBS];
-#pragma unroll
-            for (int bs = 0; bs < NBS; ++bs) s[bs] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-#pragma unroll
-                for (int bs = 0; bs < NBS; ++bs) {
-                    const int row = 32 * bs + li;
-                    const int chunk = 2 * ks + g;
-                    const u32x4 a = lds_load16(Ks + row * (2 * D) + 16 * (chunk ^ swz_k<D>(row)));
-                    s[bs] = mfma32(as_el8(a), qf[ks], s[bs]);
-                }
-            }
-
-            // Mask keys above the diagonal and past the end (straddling tiles only).
-            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
-                    }
-            }
-
-            // Online softmax, log2 domain.
-            float mx = kNegInf;
-#pragma unroll
-            for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
-            mx = max_halves(mx);
-            const float m_new = fmaxf(m_run, mx * p.c);
-            const float alpha = exp2_fast(m_run - m_new);
-            m_run = m_new;
-
-            uint32_t pp[NBS][8];
-            float lsum = 0.f;
-#pragma unroll
-            for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
-                    const float p1 = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
-                    pp[bs][r >> 1] = pack_el(p0, p1);
-                    lsum += p0 + p1;
-                }
-            l_run = fmaf(l_run, alpha, lsum);
-
-            // Deferred rescale of the unnormalized accumulator, only if some row's max moved.
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int i = 0; i < NBD; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-            }
-
-            // O^T += V^T P^T.
-            const int j16 = lane & 15;
-            const int half = (lane >> 4) & 1;
-#pragma unroll
-            for (int kk = 0; kk < KSKV; ++kk) {
-                const int bs = kk >> 1, h = kk & 1;
-                const u32x4 pv = {pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2],
-                                  pp[bs][4 * h + 3]};
-                const el8 bfrag = as_el8(pv);
-                const int row1 = 16 * kk + 4 * g + (j16 >> 2);
-                const int row2 = row1 + 8;
-#pragma unroll
-                for (int db = 0; db < NBD; ++db) {
-                    const int col = 32 * db + 16 * half + 4 * (j16 & 3);
-                    const int cchunk = col >> 3, cin = (col & 7) * 2;
-                    const s16x4 t1 = lds_load_tr(Vs + row1 * (2 * D) + 16 * (cchunk ^ swz_v<D>(row1)) + cin);
-                    const s16x4 t2 = lds_load_tr(Vs + row2 * (2 * D) + 16 * (cchunk ^ swz_v<D>(row2)) + cin);
-                    o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
-                }
-            }
-        }
-
-        if (has_next) {
-            FA2_LDS char* Kn = smem + ((j + 1) & 1) * (2 * kTileBytes);
-            ld.store(Kn, Kn + kTileBytes, tid);
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: O = O~ / l (one reciprocal per row), L = ln2 * (m + log2 l)
-    if (wave_live) {
-        const float l_tot = sum_halves(l_run);
-        const float inv = 1.0f / l_tot;
-        if (q < N) {
-            uint16_t* Orow = p.O + qhead + (size_t)q * D;
-#pragma unroll
-            for (int db = 0; db < NBD; ++db)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int d0 = 32 * db + 8 * rq + 4 * g;
-                    u32x2 w;
-                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
-                }
-            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
-        }
-    }
 }
 
 // Pipelined forward for d = 64 and 128: one workgroup = 8 wave64s = 256 query
@@ -575,6 +344,280 @@ void fwd_pipe_kernel(const FwdParams p) {
     }
 }
 
+// The pipelined forward at d = 256: the same program as fwd_pipe_kernel with
+// 32-key K/V tiles (16 KiB each, three deep per tensor), one score block per
+// step, and 4 waves (one per SIMD, 128 rows per workgroup: the O~ accumulator
+// alone takes 128 registers).
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void fwd_pipe256_kernel(const FwdParams p) {
+    constexpr int D = 256;
+    constexpr int NW = 4, ROWS = 32 * NW, BC = 32;
+    constexpr int NBS = BC / 32;         // 32-key score blocks per tile
+    constexpr int KSD = D / 16;          // MFMA reduction steps over the head dim
+    constexpr int NBD = D / 32;          // 32-wide blocks of the head dim (O^T)
+    constexpr int RB = 2 * D;            // bytes per LDS tile row
+    constexpr int kTile = BC * RB;
+    constexpr int RPI = 1024 / RB;       // tile rows per wave copy instruction
+    constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    constexpr int PERW = kTile / 1024 / NW;
+    static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile];
+    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile];
+    FA2_LDS char* const K0 = (FA2_LDS char*)Kb0;
+    FA2_LDS char* const K1 = (FA2_LDS char*)Kb1;
+    FA2_LDS char* const K2 = (FA2_LDS char*)Kb2;
+    FA2_LDS char* const V0 = (FA2_LDS char*)Vb0;
+    FA2_LDS char* const V1 = (FA2_LDS char*)Vb1;
+    FA2_LDS char* const V2 = (FA2_LDS char*)Vb2;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    const int BH = p.B * p.Hq;
+    const int level = blockIdx.x / BH;
+    const int bh = blockIdx.x - level * BH;
+    const int qtile = p.n_qtiles - 1 - level;
+    int b, hq;
+    level_head(bh, p.Hq, p.G, p.B, b, hq);
+    const int hk = hq / p.G;
+    const int N = p.N;
+    const size_t qhead = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
+    const uint16_t* Kh = p.K + khead;
+    const uint16_t* Vh = p.V + khead;
+
+    const int q0 = qtile * ROWS;
+    const int wq0 = q0 + 32 * wave;
+    const int q = wq0 + li;
+
+    el8 qf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        u32x4 v = {0, 0, 0, 0};
+        if (q < N) v = global_load16(p.Q + qhead + (size_t)q * D + 16 * ks + 8 * g);
+        qf[ks] = as_el8(v);
+    }
+
+    // Tiles the workgroup streams, and tiles this wave computes on.
+    const int n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
+    const int n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+
+    // Copy tile t of K or V into LDS.  Lane i of a copy instruction writes
+    // bytes 16*i.. of its 1 KiB (tile row R + i / CPR, 16-byte slot i % CPR),
+    // so it fetches the chunk the swizzle puts in that slot.  R is a multiple
+    // of RPI, and for these row strides swz(R + r) = swz(r) ^ swz(R) for
+    // r < RPI.  Rows past the end repeat row N-1 (their keys are masked).
+    // Byte offsets of this lane's chunks in a whole tile (held for the loop);
+    // only the tile that ends past N recomputes them, clamped.
+    uint32_t off_full[PERW];
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+        const int R = (wave * PERW + i) * RPI;
+        const int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
+        off_full[i] = (uint32_t)((R + lr) * RB + (lc ^ (16 * swz<D>(R))));
+    }
+    auto copy_tile = [&](const uint16_t* head, int t, FA2_LDS char* dst) {
+        const int kv0 = t * BC;
+        const char* base = reinterpret_cast<const char*>(head + (size_t)kv0 * D);
+        const int last = N - 1 - kv0;
+        if (last >= BC - 1) {
+#pragma unroll
+            for (int i = 0; i < PERW; ++i) copy_to_lds16(base, off_full[i], dst + (wave * PERW + i) * 1024);
+        } else {
+            int lr = lane / CPR, lc = 16 * ((lane % CPR) ^ swz<D>(lane / CPR));
+            asm volatile("" : "+v"(lr), "+v"(lc));
+#pragma unroll
+            for (int i = 0; i < PERW; ++i) {
+                const int R = (wave * PERW + i) * RPI;
+                const uint32_t off = (uint32_t)(min(R + lr, last) * RB + (lc ^ (16 * swz<D>(R))));
+                copy_to_lds16(base, off, dst + (wave * PERW + i) * 1024);
+            }
+        }
+    };
+
+    // The swizzle only flips bits 4.. of a row's byte offset below RB, so the
+    // operand addresses are a per-lane base XOR a constant: 32*ks for K rows
+    // (chunk 2*ks + g), 64*db for V columns.  The bases are rebuilt per step
+    // (opaque to the compiler) rather than holding one register per address.
+    auto scores = [&](const FA2_LDS char* Ks, f32x16 (&s)[NBS]) {
+        int kb = li * RB + 16 * (g ^ swz<D>(li));
+        asm volatile("" : "+v"(kb));
+#pragma unroll
+        for (int bs = 0; bs < NBS; ++bs) s[bs] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs) {
+                const u32x4 a = lds_load16(Ks + 32 * bs * RB + (kb ^ (32 * ks)));
+                s[bs] = mfma32(as_el8(a), qf[ks], s[bs]);
+            }
+    };
+
+    auto mask = [&](int t, f32x16 (&s)[NBS]) {
+        const int kv0 = t * BC;
+        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
+                }
+        }
+    };
+
+    f32x16 o[NBD];
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) o[i] = zero16();
+    float m_run = kNegInf;   // reference max of c * S (log2 domain), equal in lanes l and l ^ 32
+    float l_run = 0.f;       // this lane's half of the row sum, relative to m_run
+
+    // P = exp2(c S - m) in place (fp32, for the row sum) and packed to bf16
+    // (the B operand of the P V product); returns the rescale factor of O~ and l.
+    auto softmax = [&](f32x16 (&s)[NBS], uint32_t (&pp)[NBS][8]) -> float {
+        float mx = kNegInf;
+#pragma unroll
+        for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
+        mx = max_halves(mx) * p.c;
+        const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+        const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+#pragma unroll
+        for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
+                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
+                pp[bs][r >> 1] = pack_el(s[bs][r], s[bs][r + 1]);
+            }
+        return alpha;
+    };
+
+    auto row_sum = [&](const f32x16 (&pr)[NBS], float alpha) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) lsum += pr[bs][r] + pr[bs][r + 1];
+        l_run = fmaf(l_run, alpha, lsum);
+    };
+
+    // O^T += V^T P^T: V^T fragments by transposed reads of the row-major V tile
+    // (rows 16*kk + 4*g + j16/4 and +8, columns 32*db + 16*half + 4*(j16 % 4)).
+    auto pv = [&](const FA2_LDS char* Vs, const uint32_t (&pp)[NBS][8]) {
+        const int j16 = lane & 15;
+        const int x = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);    // chunk within a 32-column block
+        const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+        int vb1 = r1 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r1));
+        int vb2 = r2 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r2));
+        asm volatile("" : "+v"(vb1), "+v"(vb2));
+#pragma unroll
+        for (int kk = 0; kk < 2 * NBS; ++kk) {
+            const int bs = kk >> 1, h = kk & 1;
+            const el8 bfrag = as_el8(u32x4{pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2], pp[bs][4 * h + 3]});
+#pragma unroll
+            for (int db = 0; db < NBD; ++db) {
+                const s16x4 t1 = lds_load_tr(Vs + 16 * kk * RB + (vb1 ^ (64 * db)));
+                const s16x4 t2 = lds_load_tr(Vs + 16 * kk * RB + (vb2 ^ (64 * db)));
+                o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
+            }
+        }
+    };
+
+    // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
+    copy_tile(Kh, 0, K0);
+    copy_tile(Vh, 0, V0);
+    if (1 < n_kv) {
+        copy_tile(Kh, 1, K1);
+        copy_tile(Vh, 1, V1);
+    }
+    if (2 < n_kv) copy_tile(Kh, 2, K2);
+    wait_vm_all();
+    __syncthreads();
+    f32x16 sa[NBS], sb[NBS];       // scores of the current and the next tile, alternating
+    scores(K0, sa);
+    __syncthreads();          // K_0 is overwritten by K_3 in step 0
+
+    // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
+    // then P_j V_j.  Past a wave's last tile the step only copies; S_{j+1} of a
+    // tile the wave does not visit is computed from whatever its buffer holds
+    // and never used.
+    auto step = [&](int j, const FA2_LDS char* Ks, const FA2_LDS char* Vs, FA2_LDS char* Kw, FA2_LDS char* Vw,
+                    f32x16 (&s_cur)[NBS], f32x16 (&s_next)[NBS]) __attribute__((always_inline)) {
+        // Copies past the last tile repeat it into a released buffer that is
+        // never read, so every step issues and waits for the same count.
+        copy_tile(Kh, min(j + 3, n_kv - 1), Kw);
+        copy_tile(Vh, min(j + 2, n_kv - 1), Vw);
+        if (j < n_w) {
+            mask(j, s_cur);
+            uint32_t pp[NBS][8];
+            // Raised priority while this wave interleaves S_{j+1} with the
+            // softmax of S_j, normal for the P V products: the other wave on the
+            // SIMD then fills the matrix unit's idle slots of the mixed phase.
+            __builtin_amdgcn_s_setprio(1);
+            scores(Ks, s_next);
+            const float alpha = softmax(s_cur, pp);
+            // Materialize P here, beside the S_{j+1} products, rather than
+            // letting the compiler sink the exponentials below the branch.
+#pragma unroll
+            for (int bs = 0; bs < NBS; ++bs)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int i = 0; i < NBD; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
+            __builtin_amdgcn_s_setprio(0);
+            pv(Vs, pp);
+            row_sum(s_cur, alpha);
+        }
+        wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
+        barrier_lds();
+    };
+
+    // Unrolled by six: three buffer phases times two score arrays.  Each step
+    // after the first is guarded on its own rather than leaving the loop with
+    // a break: with six exits the compiler copied the score arrays into fixed
+    // registers at every step instead of alternating them.
+    for (int j = 0; j < n_kv; j += 6) {
+        step(j, K1, V0, K0, V2, sa, sb);
+        if (j + 1 < n_kv) step(j + 1, K2, V1, K1, V0, sb, sa);
+        if (j + 2 < n_kv) step(j + 2, K0, V2, K2, V1, sa, sb);
+        if (j + 3 < n_kv) step(j + 3, K1, V0, K0, V2, sb, sa);
+        if (j + 4 < n_kv) step(j + 4, K2, V1, K1, V0, sa, sb);
+        if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
+    }
+    wait_vm_all();
+
+    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l)
+    if (n_w > 0) {
+        const float l_tot = sum_halves(l_run);
+        const float inv = 1.0f / l_tot;
+        if (q < N) {
+            uint16_t* Orow = p.O + qhead + (size_t)q * D;
+#pragma unroll
+            for (int db = 0; db < NBD; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * db + 8 * rq + 4 * g;
+                    u32x2 w;
+                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
+                }
+            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     FwdParams arg = p;
@@ -585,10 +628,10 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
         return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL>),
                                dim3((unsigned)grid), dim3(512), args, 0, stream);
     } else {
-        arg.n_qtiles = (p.N + kFwdRows - 1) / kFwdRows;
+        arg.n_qtiles = (p.N + 127) / 128;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
-        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, CAUSAL>),
-                               dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe256_kernel<CAUSAL>),
+                               dim3((unsigned)grid), dim3(256), args, 0, stream);
     }
 }
 
