@@ -42,6 +42,15 @@
  * Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV
  * (H = Hq for Q/O/dO/dQ, H = Hkv for K/V/dK/dV); [B, Hq, N] for L and D.
  *
+ * Block-sparse attention (FlashAttention paper page, aipaper.jasonlin.tech,
+ * key contributions and limitations: attention restricted to a predefined
+ * block sparsity pattern): every entry point takes a block mask bm, NULL for
+ * dense attention, else bytes [nb, nb] with nb = ceil(N / 128), row-major by
+ * query block, shared by all batches and heads.  Scores in a zero block are
+ * masked (-inf) exactly like scores above the causal diagonal, and both
+ * masks may apply at once.  A query row left with no unmasked score has
+ * L_i = -inf, O_i = 0, D_i = 0, dQ_i = 0 and adds nothing to dK or dV.
+ *
  * Return value of every entry point: 0 on success, -1 on bad sizes
  * (negative sizes, Hq not a multiple of Hkv, d < 1 when there is work).
  */
@@ -67,11 +76,41 @@ static const double *head_ptr(const double *X, int b, int h, int H, int N, int d
     return X + (((size_t)b * H + h) * (size_t)N) * (size_t)d;
 }
 
+/*
+ * Which scores are masked: the causal mask (j > i) and, for block-sparse
+ * attention, a block mask bm [nb, nb] of 128 x 128 blocks (row-major, one
+ * byte per block, shared by every batch and head): S_ij is masked when
+ * bm[(i / 128) * nb + j / 128] == 0.  bm == NULL: no block mask.
+ */
+#define ORACLE_SPARSE_BLOCK 128
+typedef struct {
+    int causal;
+    const unsigned char *bm;
+    int nb;
+} mask_t;
+
+static int is_masked(const mask_t *mk, int i, int j)
+{
+    if (mk->causal && j > i) return 1;
+    if (mk->bm && !mk->bm[(size_t)(i / ORACLE_SPARSE_BLOCK) * mk->nb + j / ORACLE_SPARSE_BLOCK]) return 1;
+    return 0;
+}
+
+/*
+ * exp(s - L) for a row with logsumexp L.  A masked score (s = -inf) gives 0,
+ * also in a row whose every score is masked (L = -inf), where the difference
+ * itself would be undefined.
+ */
+static double prob(double s, double L)
+{
+    return s == -INFINITY ? 0.0 : exp(s - L);
+}
+
 /* Scaled, masked score S_ij of one query row q (length d) against key row k. */
 static double score(const double *q, const double *k, int d, double scale,
-                    int causal, int i, int j)
+                    const mask_t *mk, int i, int j)
 {
-    if (causal && j > i) return -INFINITY;
+    if (is_masked(mk, i, j)) return -INFINITY;
     double acc = 0.0;
     for (int t = 0; t < d; ++t) acc += q[t] * k[t];
     return scale * acc;
@@ -79,18 +118,20 @@ static double score(const double *q, const double *k, int d, double scale,
 
 /*
  * Row i of one head: fills s[0..N) with the scaled masked scores and returns
- * L_i = m + ln sum_j exp(s_j - m).  The causal mask keeps j <= i, so every
- * row has at least one finite score (j = 0).
+ * L_i = m + ln sum_j exp(s_j - m).  The causal mask alone keeps j = 0; a
+ * block mask can mask a whole row, whose logsumexp over no terms is -inf
+ * (its output row is then 0 and it contributes nothing to any gradient).
  */
 static double row_scores_lse(const double *Qh, const double *Kh, int N, int d,
-                             double scale, int causal, int i, double *s)
+                             double scale, const mask_t *mk, int i, double *s)
 {
     const double *q = Qh + (size_t)i * d;
     double m = -INFINITY;
     for (int j = 0; j < N; ++j) {
-        s[j] = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
+        s[j] = score(q, Kh + (size_t)j * d, d, scale, mk, i, j);
         if (s[j] > m) m = s[j];
     }
+    if (m == -INFINITY) return -INFINITY;
     double sum = 0.0;
     for (int j = 0; j < N; ++j) sum += exp(s[j] - m);
     return m + log(sum);
@@ -98,13 +139,13 @@ static double row_scores_lse(const double *Qh, const double *Kh, int N, int d,
 
 /* Forward of one query row: O_i (length d) and L_i. */
 static double row_forward(const double *Qh, const double *Kh, const double *Vh,
-                          int N, int d, double scale, int causal, int i,
+                          int N, int d, double scale, const mask_t *mk, int i,
                           double *s, double *o)
 {
-    double L = row_scores_lse(Qh, Kh, N, d, scale, causal, i, s);
+    double L = row_scores_lse(Qh, Kh, N, d, scale, mk, i, s);
     for (int t = 0; t < d; ++t) o[t] = 0.0;
     for (int j = 0; j < N; ++j) {
-        double p = exp(s[j] - L);
+        double p = prob(s[j], L);
         if (p == 0.0) continue;              /* masked (exp(-inf) = 0) */
         const double *v = Vh + (size_t)j * d;
         for (int t = 0; t < d; ++t) o[t] += p * v[t];
@@ -113,9 +154,10 @@ static double row_forward(const double *Qh, const double *Kh, const double *Vh,
 }
 
 int oracle_fwd(const double *Q, const double *K, const double *V, double *O,
-               double *L, int B, int Hq, int Hkv, int N, int d, int causal,
+               double *L, int B, int Hq, int Hkv, int N, int d, int causal, const unsigned char *bm,
                double scale)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if ((long)B * Hq * N == 0) return 0;
     const int G = Hq / Hkv;
@@ -132,7 +174,7 @@ int oracle_fwd(const double *Q, const double *K, const double *V, double *O,
             const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);
             const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);
             double *o = O + (size_t)r * d;
-            double l = row_forward(Qh, Kh, Vh, N, d, scale, causal, i, s, o);
+            double l = row_forward(Qh, Kh, Vh, N, d, scale, &mk, i, s, o);
             if (L) L[r] = l;
         }
         free(s);
@@ -146,10 +188,11 @@ int oracle_fwd(const double *Q, const double *K, const double *V, double *O,
  * outputs of large problems one row at a time.
  */
 int oracle_fwd_rows(const double *Q, const double *K, const double *V,
-                    int B, int Hq, int Hkv, int N, int d, int causal,
+                    int B, int Hq, int Hkv, int N, int d, int causal, const unsigned char *bm,
                     double scale, int n, const int *rb, const int *rh,
                     const int *ri, double *O_rows, double *L_rows)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     for (int r = 0; r < n; ++r)
         if (rb[r] < 0 || rb[r] >= B || rh[r] < 0 || rh[r] >= Hq ||
@@ -164,7 +207,7 @@ int oracle_fwd_rows(const double *Q, const double *K, const double *V,
             const double *Qh = head_ptr(Q, rb[r], rh[r], Hq, N, d);
             const double *Kh = head_ptr(K, rb[r], rh[r] / G, Hkv, N, d);
             const double *Vh = head_ptr(V, rb[r], rh[r] / G, Hkv, N, d);
-            double l = row_forward(Qh, Kh, Vh, N, d, scale, causal, ri[r], s,
+            double l = row_forward(Qh, Kh, Vh, N, d, scale, &mk, ri[r], s,
                                    O_rows + (size_t)r * d);
             if (L_rows) L_rows[r] = l;
         }
@@ -183,7 +226,7 @@ int oracle_fwd_rows(const double *Q, const double *K, const double *V,
  */
 static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
                             const double *dO, int Hq, int Hkv, int N, int d,
-                            int causal, double scale, int b, int hk,
+                            const mask_t *mk, double scale, int b, int hk,
                             double *dQg, double *dKh, double *dVh,
                             double *Lg, double *Dg)
 {
@@ -203,10 +246,10 @@ static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
             int hq = hk * G + g;
             const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
             const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
-            double L = row_scores_lse(Qh, Kh, N, d, scale, causal, i, s);
+            double L = row_scores_lse(Qh, Kh, N, d, scale, mk, i, s);
             double D = 0.0;
             for (int j = 0; j < N; ++j) {
-                double p = exp(s[j] - L);
+                double p = prob(s[j], L);
                 if (p == 0.0) continue;
                 const double *v = Vh + (size_t)j * d;
                 double dp = 0.0;
@@ -230,8 +273,8 @@ static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
             double *dq = dQg + (size_t)r * d;
             for (int t = 0; t < d; ++t) dq[t] = 0.0;
             for (int j = 0; j < N; ++j) {
-                double sij = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
-                double p = exp(sij - Lst[r]);
+                double sij = score(q, Kh + (size_t)j * d, d, scale, mk, i, j);
+                double p = prob(sij, Lst[r]);
                 if (p == 0.0) continue;
                 const double *v = Vh + (size_t)j * d;
                 double dp = 0.0;
@@ -257,8 +300,8 @@ static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
             const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
             for (int i = 0; i < N; ++i) {
                 const double *q = Qh + (size_t)i * d;
-                double sij = score(q, k, d, scale, causal, i, j);
-                double p = exp(sij - Lst[(long)g * N + i]);
+                double sij = score(q, k, d, scale, mk, i, j);
+                double p = prob(sij, Lst[(long)g * N + i]);
                 if (p == 0.0) continue;
                 const double *dOr = dOh + (size_t)i * d;
                 double dp = 0.0;
@@ -281,9 +324,10 @@ static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
 
 int oracle_bwd(const double *Q, const double *K, const double *V,
                const double *dO, double *dQ, double *dK, double *dV,
-               double *D, int B, int Hq, int Hkv, int N, int d, int causal,
+               double *D, int B, int Hq, int Hkv, int N, int d, int causal, const unsigned char *bm,
                double scale)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if ((long)B * Hq * N == 0) return 0;
     const int G = Hq / Hkv;
@@ -292,7 +336,7 @@ int oracle_bwd(const double *Q, const double *K, const double *V,
             size_t qoff = (((size_t)b * Hq + (size_t)hk * G) * N) * d;
             size_t koff = (((size_t)b * Hkv + hk) * (size_t)N) * d;
             double *Dg = D ? D + ((size_t)b * Hq + (size_t)hk * G) * N : NULL;
-            bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+            bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk,
                             dQ + qoff, dK + koff, dV + koff, NULL, Dg);
         }
     return 0;
@@ -305,13 +349,14 @@ int oracle_bwd(const double *Q, const double *K, const double *V,
  */
 int oracle_bwd_head(const double *Q, const double *K, const double *V,
                     const double *dO, int B, int Hq, int Hkv, int N, int d,
-                    int causal, double scale, int b, int hk, double *dQg,
+                    int causal, const unsigned char *bm, double scale, int b, int hk, double *dQg,
                     double *dKh, double *dVh, double *Lg, double *Dg)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if (b < 0 || b >= B || hk < 0 || hk >= Hkv) return -1;
     if (N == 0) return 0;
-    bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+    bwd_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk,
                     dQg, dKh, dVh, Lg, Dg);
     return 0;
 }
@@ -348,17 +393,18 @@ static double round_bf16(double x)
 
 /* Forward row at the working precision: O_i (unrounded) from bf16(p_ij), and L_i. */
 static double row_forward_bf16(const double *Qh, const double *Kh, const double *Vh,
-                               int N, int d, double scale, int causal, int i,
+                               int N, int d, double scale, const mask_t *mk, int i,
                                double *s, double *o)
 {
     const double *q = Qh + (size_t)i * d;
     double m = -INFINITY;
     for (int j = 0; j < N; ++j) {
-        s[j] = score(q, Kh + (size_t)j * d, d, scale, causal, i, j);
+        s[j] = score(q, Kh + (size_t)j * d, d, scale, mk, i, j);
         if (s[j] > m) m = s[j];
     }
     double l = 0.0;
     for (int t = 0; t < d; ++t) o[t] = 0.0;
+    if (m == -INFINITY) return -INFINITY;    /* every score masked: O_i = 0 */
     for (int j = 0; j < N; ++j) {
         double p = exp(s[j] - m);
         l += p;
@@ -372,9 +418,10 @@ static double row_forward_bf16(const double *Qh, const double *Kh, const double 
 }
 
 int oracle_fwd_bf16(const double *Q, const double *K, const double *V, double *O,
-                    double *L, int B, int Hq, int Hkv, int N, int d, int causal,
+                    double *L, int B, int Hq, int Hkv, int N, int d, int causal, const unsigned char *bm,
                     double scale)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if ((long)B * Hq * N == 0) return 0;
     const int G = Hq / Hkv;
@@ -390,7 +437,7 @@ int oracle_fwd_bf16(const double *Q, const double *K, const double *V, double *O
             const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
             const double *Kh = head_ptr(K, b, hq / G, Hkv, N, d);
             const double *Vh = head_ptr(V, b, hq / G, Hkv, N, d);
-            double l = row_forward_bf16(Qh, Kh, Vh, N, d, scale, causal, i, s, O + (size_t)r * d);
+            double l = row_forward_bf16(Qh, Kh, Vh, N, d, scale, &mk, i, s, O + (size_t)r * d);
             if (L) L[r] = l;
         }
         free(s);
@@ -402,7 +449,7 @@ int oracle_fwd_bf16(const double *Q, const double *K, const double *V, double *O
  * query heads hk*G.., dKh and dVh [N,d]. */
 static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double *V,
                                  const double *dO, int Hq, int Hkv, int N, int d,
-                                 int causal, double scale, int b, int hk,
+                                 const mask_t *mk, double scale, int b, int hk,
                                  double *dQg, double *dKh, double *dVh, double *Dg)
 {
     const int G = Hq / Hkv;
@@ -421,7 +468,7 @@ static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double 
             int hq = hk * G + g;
             const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
             const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
-            Lst[r] = row_forward_bf16(Qh, Kh, Vh, N, d, scale, causal, i, s, o);
+            Lst[r] = row_forward_bf16(Qh, Kh, Vh, N, d, scale, mk, i, s, o);
             double D = 0.0;
             for (int t = 0; t < d; ++t) D += dOr[t] * round_bf16(o[t]);
             Dst[r] = D;
@@ -439,7 +486,7 @@ static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double 
         double *dq = dQg + (size_t)r * d;
         for (int t = 0; t < d; ++t) dq[t] = 0.0;
         for (int j = 0; j < N; ++j) {
-            double p = exp(score(q, Kh + (size_t)j * d, d, scale, causal, i, j) - Lst[r]);
+            double p = prob(score(q, Kh + (size_t)j * d, d, scale, mk, i, j), Lst[r]);
             if (p == 0.0) continue;
             const double *v = Vh + (size_t)j * d;
             double dp = 0.0;
@@ -464,7 +511,7 @@ static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double 
             const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
             for (int i = 0; i < N; ++i) {
                 const double *q = Qh + (size_t)i * d;
-                double p = exp(score(q, k, d, scale, causal, i, j) - Lst[(long)g * N + i]);
+                double p = prob(score(q, k, d, scale, mk, i, j), Lst[(long)g * N + i]);
                 if (p == 0.0) continue;
                 const double *dOr = dOh + (size_t)i * d;
                 double dp = 0.0;
@@ -486,8 +533,9 @@ static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double 
 
 int oracle_bwd_bf16(const double *Q, const double *K, const double *V,
                     const double *dO, double *dQ, double *dK, double *dV, double *D,
-                    int B, int Hq, int Hkv, int N, int d, int causal, double scale)
+                    int B, int Hq, int Hkv, int N, int d, int causal, const unsigned char *bm, double scale)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if ((long)B * Hq * N == 0) return 0;
     const int G = Hq / Hkv;
@@ -496,7 +544,7 @@ int oracle_bwd_bf16(const double *Q, const double *K, const double *V,
             size_t qoff = (((size_t)b * Hq + (size_t)hk * G) * N) * d;
             size_t koff = (((size_t)b * Hkv + hk) * (size_t)N) * d;
             double *Dg = D ? D + ((size_t)b * Hq + (size_t)hk * G) * N : NULL;
-            bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk,
+            bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk,
                                  dQ + qoff, dK + koff, dV + koff, Dg);
         }
     return 0;
@@ -504,13 +552,14 @@ int oracle_bwd_bf16(const double *Q, const double *K, const double *V,
 
 int oracle_bwd_bf16_head(const double *Q, const double *K, const double *V,
                          const double *dO, int B, int Hq, int Hkv, int N, int d,
-                         int causal, double scale, int b, int hk, double *dQg,
+                         int causal, const unsigned char *bm, double scale, int b, int hk, double *dQg,
                          double *dKh, double *dVh)
 {
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
     if (check_sizes(B, Hq, Hkv, N, d)) return -1;
     if (b < 0 || b >= B || hk < 0 || hk >= Hkv) return -1;
     if (N == 0) return 0;
-    bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, causal, scale, b, hk, dQg, dKh, dVh, NULL);
+    bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk, dQg, dKh, dVh, NULL);
     return 0;
 }
 

@@ -9,7 +9,10 @@ gradients dQ, dK, dV of sum(dO * O)) in double precision, following the
 FlashAttention-2 summary page (zhaifeiyue.github.io), section 3 "Target
 operation" and section 4's symbol table and checks.  Every function takes
 float64 arrays in [B, H, N, d] layout (any values; bf16 inputs are passed as
-their exact float64 values).
+their exact float64 values).  ``block_mask`` (optional, every function):
+a [ceil(N/128), ceil(N/128)] array, nonzero where a 128-row block of queries
+may attend to a 128-key block (block-sparse attention, shared by all batches
+and heads); see oracle.c for the convention on rows it masks entirely.
 """
 from __future__ import annotations
 
@@ -41,17 +44,18 @@ def _open(path: str):
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int)
     i = ctypes.c_int
-    lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
-    lib.oracle_fwd_rows.argtypes = [dp, dp, dp, i, i, i, i, i, i, ctypes.c_double,
+    bm = ctypes.c_void_p          # block mask bytes, or None
+    lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double]
+    lib.oracle_fwd_rows.argtypes = [dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double,
                                     i, ip, ip, ip, dp, dp]
-    lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i,
+    lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, bm,
                                ctypes.c_double]
-    lib.oracle_bwd_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double,
+    lib.oracle_bwd_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double,
                                     i, i, dp, dp, dp, dp, dp]
-    lib.oracle_fwd_bf16.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
-    lib.oracle_bwd_bf16.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i,
+    lib.oracle_fwd_bf16.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double]
+    lib.oracle_bwd_bf16.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, bm,
                                     ctypes.c_double]
-    lib.oracle_bwd_bf16_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double,
+    lib.oracle_bwd_bf16_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double,
                                          i, i, dp, dp, dp]
     for f in (lib.oracle_fwd, lib.oracle_fwd_rows, lib.oracle_bwd, lib.oracle_bwd_head,
               lib.oracle_fwd_bf16, lib.oracle_bwd_bf16, lib.oracle_bwd_bf16_head):
@@ -95,6 +99,24 @@ def _dims(q: np.ndarray, k: np.ndarray):
     return B, Hq, Hkv, N, d
 
 
+SPARSE_BLOCK = 128   # rows and keys per block of a block-sparse mask
+
+
+def _mask(block_mask, N: int):
+    """Block mask as contiguous uint8 [ceil(N/128), ceil(N/128)] (None: dense)."""
+    if block_mask is None:
+        return None
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    m = np.ascontiguousarray(np.asarray(block_mask) != 0, dtype=np.uint8)
+    if m.shape != (nb, nb):
+        raise ValueError(f"block mask shape {m.shape}, expected {(nb, nb)}")
+    return m
+
+
+def _mptr(m):
+    return None if m is None else m.ctypes.data
+
+
 def default_scale(d: int) -> float:
     return 1.0 / np.sqrt(d)
 
@@ -103,23 +125,24 @@ def num_threads(lib=None) -> int:
     return (lib or load()).oracle_num_threads()
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, lib=None):
+def forward(q, k, v, causal: bool = False, scale: float | None = None, lib=None, block_mask=None):
     """Full forward: returns (O [B,Hq,N,d], L [B,Hq,N]) in float64."""
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     if scale is None:
         scale = default_scale(d)
     o = np.empty_like(q)
     L = np.empty((B, Hq, N), dtype=np.float64)
     rc = lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
-                        B, Hq, Hkv, N, d, int(causal), float(scale))
+                        B, Hq, Hkv, N, d, int(causal), _mptr(bm), float(scale))
     if rc != 0:
         raise ValueError("oracle_fwd: bad sizes")
     return o, L
 
 
-def forward_rows(q, k, v, rows, causal: bool = False, scale: float | None = None, lib=None):
+def forward_rows(q, k, v, rows, causal: bool = False, scale: float | None = None, lib=None, block_mask=None):
     """Forward for selected rows.  ``rows`` is an int array [n, 3] of (b, hq, i).
 
     Returns (O_rows [n, d], L_rows [n]) in float64.
@@ -127,6 +150,7 @@ def forward_rows(q, k, v, rows, causal: bool = False, scale: float | None = None
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     if scale is None:
         scale = default_scale(d)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
@@ -137,7 +161,7 @@ def forward_rows(q, k, v, rows, causal: bool = False, scale: float | None = None
     o = np.empty((n, d), dtype=np.float64)
     L = np.empty((n,), dtype=np.float64)
     ip = ctypes.POINTER(ctypes.c_int)
-    rc = lib.oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, int(causal),
+    rc = lib.oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, int(causal), _mptr(bm),
                              float(scale), n, rb.ctypes.data_as(ip), rh.ctypes.data_as(ip),
                              ri.ctypes.data_as(ip), _ptr(o), _ptr(L))
     if rc != 0:
@@ -145,11 +169,12 @@ def forward_rows(q, k, v, rows, causal: bool = False, scale: float | None = None
     return o, L
 
 
-def backward(q, k, v, do, causal: bool = False, scale: float | None = None, lib=None):
+def backward(q, k, v, do, causal: bool = False, scale: float | None = None, lib=None, block_mask=None):
     """Full backward: returns (dQ, dK, dV, D) in float64 (D is [B,Hq,N])."""
     lib = lib or load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     if scale is None:
         scale = default_scale(d)
     dq = np.empty_like(q)
@@ -157,14 +182,14 @@ def backward(q, k, v, do, causal: bool = False, scale: float | None = None, lib=
     dv = np.empty_like(v)
     D = np.empty((B, Hq, N), dtype=np.float64)
     rc = lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(D), B, Hq, Hkv, N, d, int(causal), float(scale))
+                        _ptr(D), B, Hq, Hkv, N, d, int(causal), _mptr(bm), float(scale))
     if rc != 0:
         raise ValueError("oracle_bwd: bad sizes")
     return dq, dk, dv, D
 
 
 def backward_head(q, k, v, do, b: int, hk: int, causal: bool = False,
-                  scale: float | None = None, lib=None):
+                  scale: float | None = None, lib=None, block_mask=None):
     """Backward of key/value head (b, hk) only.
 
     Returns (dQ [G,N,d] for query heads hk*G.., dK [N,d], dV [N,d], L [G,N], D [G,N]).
@@ -172,6 +197,7 @@ def backward_head(q, k, v, do, b: int, hk: int, causal: bool = False,
     lib = lib or load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     G = Hq // Hkv
     if scale is None:
         scale = default_scale(d)
@@ -181,35 +207,37 @@ def backward_head(q, k, v, do, b: int, hk: int, causal: bool = False,
     L = np.empty((G, N), dtype=np.float64)
     D = np.empty((G, N), dtype=np.float64)
     rc = lib.oracle_bwd_head(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, Hq, Hkv, N, d,
-                             int(causal), float(scale), int(b), int(hk), _ptr(dq),
+                             int(causal), _mptr(bm), float(scale), int(b), int(hk), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(L), _ptr(D))
     if rc != 0:
         raise ValueError("oracle_bwd_head: bad sizes or head index")
     return dq, dk, dv, L, D
 
 
-def forward_bf16(q, k, v, causal: bool = False, scale: float | None = None, lib=None):
+def forward_bf16(q, k, v, causal: bool = False, scale: float | None = None, lib=None, block_mask=None):
     """The forward at the method's working precision (bf16 P in P V): (O unrounded, L)."""
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     if scale is None:
         scale = default_scale(d)
     o = np.empty_like(q)
     L = np.empty((B, Hq, N), dtype=np.float64)
     rc = lib.oracle_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
-                             B, Hq, Hkv, N, d, int(causal), float(scale))
+                             B, Hq, Hkv, N, d, int(causal), _mptr(bm), float(scale))
     if rc != 0:
         raise ValueError("oracle_fwd_bf16: bad sizes")
     return o, L
 
 
-def backward_bf16(q, k, v, do, causal: bool = False, scale: float | None = None, lib=None,
+def backward_bf16(q, k, v, do, causal: bool = False, scale: float | None = None, lib=None, block_mask=None,
                   return_d: bool = False):
     """The backward at the method's working precision: (dQ, dK, dV) unrounded (and D)."""
     lib = lib or load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     if scale is None:
         scale = default_scale(d)
     dq = np.empty_like(q)
@@ -217,18 +245,19 @@ def backward_bf16(q, k, v, do, causal: bool = False, scale: float | None = None,
     dv = np.empty_like(v)
     D = np.empty((B, Hq, N), dtype=np.float64)
     rc = lib.oracle_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                             _ptr(D), B, Hq, Hkv, N, d, int(causal), float(scale))
+                             _ptr(D), B, Hq, Hkv, N, d, int(causal), _mptr(bm), float(scale))
     if rc != 0:
         raise ValueError("oracle_bwd_bf16: bad sizes")
     return (dq, dk, dv, D) if return_d else (dq, dk, dv)
 
 
 def backward_bf16_head(q, k, v, do, b: int, hk: int, causal: bool = False,
-                       scale: float | None = None, lib=None):
+                       scale: float | None = None, lib=None, block_mask=None):
     """Working-precision backward of key/value head (b, hk): (dQ [G,N,d], dK [N,d], dV [N,d])."""
     lib = lib or load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Hq, Hkv, N, d = _dims(q, k)
+    bm = _mask(block_mask, N)
     G = Hq // Hkv
     if scale is None:
         scale = default_scale(d)
@@ -236,7 +265,7 @@ def backward_bf16_head(q, k, v, do, b: int, hk: int, causal: bool = False,
     dk = np.empty((N, d), dtype=np.float64)
     dv = np.empty((N, d), dtype=np.float64)
     rc = lib.oracle_bwd_bf16_head(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, Hq, Hkv, N, d,
-                                  int(causal), float(scale), int(b), int(hk), _ptr(dq),
+                                  int(causal), _mptr(bm), float(scale), int(b), int(hk), _ptr(dq),
                                   _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle_bwd_bf16_head: bad sizes or head index")

@@ -11,7 +11,10 @@ AssertionError when the oracle disagrees with:
   moves at every key),
 - invariants of the definition (rows of P sum to one, constant V, shifting
   keys, permuting keys, GQA equals repeated K/V heads, column sums of dV,
-  causal row 0, D = rowsum(dO * O)).
+  causal row 0, D = rowsum(dO * O)),
+- for block-sparse attention, PyTorch with the equivalent element mask,
+  dense attention (all-ones mask) and attention over a subset of the rows
+  (rows the mask empties).
 
 The definition pinned is O = softmax(scale * Q K^T [+ causal mask]) V with
 L = m + ln(l) and D = rowsum(dO o O) (FlashAttention-2 summary page,
@@ -385,6 +388,122 @@ def pin_working_precision(lib):
         _close(hv_, dv_b2[0, 0], 0, "bf16 head dV")
 
 
+# ----------------------------------------------------------------------------
+# 7. block-sparse attention
+# ----------------------------------------------------------------------------
+def _element_mask(block_mask, N, causal):
+    """Allowed (query, key) pairs: the block mask expanded to elements, and the causal mask."""
+    bs = orc.SPARSE_BLOCK
+    idx = np.arange(N) // bs
+    allowed = np.asarray(block_mask, dtype=bool)[idx[:, None], idx[None, :]]
+    if causal:
+        allowed &= np.tril(np.ones((N, N), dtype=bool))
+    return allowed
+
+
+def _torch_masked(q, k, v, do, allowed, scale):
+    """PyTorch CPU float64 attention with an explicit boolean mask, and its gradients."""
+    import torch
+    import torch.nn.functional as F
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    m = torch.tensor(allowed)
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale, enable_gqa=(G > 1))
+    with torch.no_grad():
+        kr = tk.repeat_interleave(G, dim=1)
+        sc = scale * torch.matmul(tq, kr.transpose(-1, -2).contiguous())
+        lse = torch.logsumexp(sc.masked_fill(~m, float("-inf")), dim=-1)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return (o.detach().numpy(), lse.numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())
+
+
+def pin_block_sparse(lib):
+    """Block masks against PyTorch with the equivalent element mask (asymmetric masks, so a
+    transposed or ignored mask fails), all-ones masks against dense attention, and rows the
+    mask empties (L = -inf, O = 0, no gradient) against attention over the other rows."""
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, N, d = 1, 2, 1, 300, 4          # 3 x 3 blocks, the last one ragged
+    q, k, v = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    do = _rand(rng, B, Hq, N, d)
+    scale = 0.8
+    masks = {
+        "lower-left": np.array([[1, 0, 0], [1, 1, 0], [0, 1, 1]]),
+        "upper": np.array([[0, 1, 1], [0, 0, 1], [1, 0, 0]]),
+        "column 0": np.array([[1, 0, 0], [1, 0, 0], [1, 0, 0]]),
+    }
+    for name, bm in masks.items():
+        for causal in (False, True):
+            allowed = _element_mask(bm, N, causal)
+            if not allowed.any(axis=1).all():
+                continue                         # rows with no key: checked below
+            case = f"{name} causal{int(causal)}"
+            o, L = orc.forward(q, k, v, causal, scale, lib=lib, block_mask=bm)
+            dq, dk, dv, D = orc.backward(q, k, v, do, causal, scale, lib=lib, block_mask=bm)
+            to, tL, tdq, tdk, tdv = _torch_masked(q, k, v, do, allowed, scale)
+            _close(o, to, 1e-12, f"block-sparse O {case}")
+            _close(L, tL, 1e-12, f"block-sparse L {case}")
+            _close(dq, tdq, 1e-11, f"block-sparse dQ {case}")
+            _close(dk, tdk, 1e-11, f"block-sparse dK {case}")
+            _close(dv, tdv, 1e-11, f"block-sparse dV {case}")
+            _close(D, np.sum(do * to, axis=-1), 1e-12, f"block-sparse D {case}")
+
+    ones = np.ones((3, 3))
+    for causal in (False, True):
+        o, L = orc.forward(q, k, v, causal, scale, lib=lib, block_mask=ones)
+        o0, L0 = orc.forward(q, k, v, causal, scale, lib=lib)
+        _close(o, o0, 0, "all-ones block mask O")
+        _close(L, L0, 0, "all-ones block mask L")
+        g = orc.backward(q, k, v, do, causal, scale, lib=lib, block_mask=ones)
+        g0 = orc.backward(q, k, v, do, causal, scale, lib=lib)
+        for a, b_, n in zip(g, g0, ("dQ", "dK", "dV", "D")):
+            _close(a, b_, 0, f"all-ones block mask {n}")
+
+    # Query block 1 (rows 128..255) masked entirely; causal too, so that block 0
+    # attends only to itself.
+    bm = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 1]])
+    for causal in (False, True):
+        case = f"empty query block causal{int(causal)}"
+        o, L = orc.forward(q, k, v, causal, scale, lib=lib, block_mask=bm)
+        dq, dk, dv, D = orc.backward(q, k, v, do, causal, scale, lib=lib, block_mask=bm)
+        empty = slice(128, 256)
+        assert np.all(L[:, :, empty] == -np.inf), f"{case}: L of masked rows"
+        assert np.all(o[:, :, empty] == 0.0), f"{case}: O of masked rows"
+        assert np.all(dq[:, :, empty] == 0.0), f"{case}: dQ of masked rows"
+        assert np.all(D[:, :, empty] == 0.0), f"{case}: D of masked rows"
+        keep = np.r_[0:128, 256:N]
+        allowed = _element_mask(bm, N, causal)[keep]
+        to, tL, tdq, tdk, tdv = _torch_masked(q[:, :, keep], k, v, do[:, :, keep], allowed, scale)
+        _close(o[:, :, keep], to, 1e-12, f"{case}: O of the other rows")
+        _close(L[:, :, keep], tL, 1e-12, f"{case}: L of the other rows")
+        _close(dq[:, :, keep], tdq, 1e-11, f"{case}: dQ of the other rows")
+        _close(dk, tdk, 1e-11, f"{case}: dK")
+        _close(dv, tdv, 1e-11, f"{case}: dV")
+        # The working-precision variants: the same empty rows, and within bf16
+        # rounding of the exact values elsewhere.
+        ob, Lb = orc.forward_bf16(q, k, v, causal, scale, lib=lib, block_mask=bm)
+        assert np.all(Lb[:, :, empty] == -np.inf) and np.all(ob[:, :, empty] == 0.0), \
+            f"{case}: working-precision forward of masked rows"
+        _close(ob[:, :, keep], o[:, :, keep], 2e-2, f"{case}: working-precision O")
+        wq, wk, wv = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib, block_mask=bm)
+        assert np.all(wq[:, :, empty] == 0.0), f"{case}: working-precision dQ of masked rows"
+        _close(wq, dq, 5e-2, f"{case}: working-precision dQ")
+        _close(wk, dk, 5e-2, f"{case}: working-precision dK")
+        _close(wv, dv, 5e-2, f"{case}: working-precision dV")
+        # Row and head entry points agree with the full ones.
+        rows = np.array([[0, 1, 5], [0, 0, 130], [0, 1, 299]])
+        orow, Lrow = orc.forward_rows(q, k, v, rows, causal, scale, lib=lib, block_mask=bm)
+        assert Lrow[1] == -np.inf and np.all(orow[1] == 0.0), f"{case}: forward_rows masked row"
+        _close(orow[[0, 2]], o[0, rows[[0, 2], 1], rows[[0, 2], 2]], 0, f"{case}: forward_rows")
+        hq_, hk_, hv_, _, _ = orc.backward_head(q, k, v, do, 0, 0, causal, scale, lib=lib,
+                                                block_mask=bm)
+        _close(hq_, dq[0], 0, f"{case}: backward_head dQ")
+        _close(hk_, dk[0, 0], 0, f"{case}: backward_head dK")
+        bq_, bk_, bv_ = orc.backward_bf16_head(q, k, v, do, 0, 0, causal, scale, lib=lib,
+                                               block_mask=bm)
+        _close(bq_, wq[0], 0, f"{case}: backward_bf16_head dQ")
+        _close(bv_, wv[0, 0], 0, f"{case}: backward_bf16_head dV")
+
+
 ALL_PINS = [pin_golden_two_key, pin_torch_forward, pin_torch_backward,
             pin_finite_differences, pin_closed_forms, pin_invariants,
-            pin_sampled_entry_points, pin_working_precision]
+            pin_sampled_entry_points, pin_working_precision, pin_block_sparse]

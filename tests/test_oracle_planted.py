@@ -17,8 +17,18 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 MUTATIONS = [
     ("scale dropped from the scores", "return scale * acc;", "return acc;"),
-    ("causal mask off by one", "if (causal && j > i) return -INFINITY;",
-     "if (causal && j > i + 1) return -INFINITY;"),
+    ("causal mask off by one", "if (mk->causal && j > i) return 1;",
+     "if (mk->causal && j > i + 1) return 1;"),
+    ("block mask ignored", "if (mk->bm && !mk->bm[", "if (0 && mk->bm && !mk->bm["),
+    ("block mask transposed",
+     "mk->bm[(size_t)(i / ORACLE_SPARSE_BLOCK) * mk->nb + j / ORACLE_SPARSE_BLOCK]",
+     "mk->bm[(size_t)(j / ORACLE_SPARSE_BLOCK) * mk->nb + i / ORACLE_SPARSE_BLOCK]"),
+    ("masked row: exp(s - L) taken at s = L = -inf", "return s == -INFINITY ? 0.0 : exp(s - L);",
+     "return exp(s - L);"),
+    ("masked row: L = 0 instead of -inf", "if (m == -INFINITY) return -INFINITY;\n    double sum",
+     "if (m == -INFINITY) return 0.0;\n    double sum"),
+    ("masked row of the working-precision forward divided by l = 0",
+     "if (m == -INFINITY) return -INFINITY;    /* every score masked: O_i = 0 */", ""),
     ("log2 instead of natural log in L", "return m + log(sum);", "return m + log2(sum);"),
     ("row maximum not subtracted inside the sum", "sum += exp(s[j] - m);", "sum += exp(s[j]);"),
     ("wrong GQA head mapping in the forward",
