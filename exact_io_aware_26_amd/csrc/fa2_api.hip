@@ -160,6 +160,21 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
     return FA2_OK;
 }
 
+// Block-sparse attention: the block mask [nb, nb] bytes, nb = ceil(N / 128).
+// It must be present, d must be 64 or 128, N at most kSparseMaxN (the kernels
+// hold one mask row or column of tiles in LDS), and no output may overlap it.
+fa2_status validate_mask(const unsigned char* bmask, int N, int d, const void* const* outs,
+                         const uint64_t* out_bytes, int n_outs) {
+    if (!bmask) return fail(FA2_ERR_INVALID_ARGUMENT, "block_mask is NULL");
+    if (d != 64 && d != 128) return fail(FA2_ERR_UNSUPPORTED, "block-sparse attention needs d = 64 or 128");
+    if (N > fa2::kSparseMaxN) return fail(FA2_ERR_UNSUPPORTED, "block-sparse attention needs N <= 262144");
+    const uint64_t nb = (uint64_t)((N + fa2::kSparseBlock - 1) / fa2::kSparseBlock);
+    for (int o = 0; o < n_outs; ++o)
+        if (overlaps(outs[o], out_bytes[o], bmask, nb * nb))
+            return fail(FA2_ERR_INVALID_ARGUMENT, "an output aliases block_mask");
+    return FA2_OK;
+}
+
 constexpr double kLog2e = 1.4426950408889634074;
 
 }  // namespace
@@ -216,13 +231,22 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 namespace {
 
 // The forward for either element format (f16: the kernels compiled into fa2_f16).
-fa2_status fwd_impl(bool f16, const void* Q, const void* K, const void* V, void* O, float* L, int B,
-                    int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
+// bmask: NULL for dense attention; `sparse` says whether the caller is a
+// block-sparse entry point (which then requires a mask).
+fa2_status fwd_impl(bool f16, bool sparse, const unsigned char* bmask, const void* Q, const void* K,
+                    const void* V, void* O, float* L, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float scale, void* stream) {
     g_last_error[0] = '\0';
     bool empty;
     Sizes sz;
     fa2_status s = validate_fwd(Q, K, V, O, L, B, Hq, Hkv, N, d, scale, &empty, &sz);
     if (s != FA2_OK || empty) return s;
+    if (sparse) {
+        const void* outs[2] = {O, L};
+        const uint64_t ob[2] = {sz.q_elems * 2, sz.rows * 4};
+        s = validate_mask(bmask, N, d, outs, ob, 2);
+        if (s != FA2_OK) return s;
+    }
     fa2::FwdParams p;
     p.Q = static_cast<const uint16_t*>(Q);
     p.K = static_cast<const uint16_t*>(K);
@@ -236,6 +260,8 @@ fa2_status fwd_impl(bool f16, const void* Q, const void* K, const void* V, void*
     p.G = Hq / Hkv;
     p.n_qtiles = (N + fa2::kFwdRows - 1) / fa2::kFwdRows;
     p.c = (float)((double)scale * kLog2e);
+    p.bmask = sparse ? bmask : nullptr;
+    p.nb = (N + fa2::kSparseBlock - 1) / fa2::kSparseBlock;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = f16 ? fa2_f16::launch_fwd(p, d, causal != 0, st) : fa2::launch_fwd(p, d, causal != 0, st);
     if (e != hipSuccess) return fail(FA2_ERR_HIP, "%s", hipGetErrorString(e));
@@ -243,10 +269,11 @@ fa2_status fwd_impl(bool f16, const void* Q, const void* K, const void* V, void*
 }
 
 // The backward stages for either element format.
-fa2_status bwd_impl(bool f16, unsigned stages, const void* Q, const void* K, const void* V,
-                    const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
-                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
-                    int causal, float scale, void* stream) {
+fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char* bmask,
+                    const void* Q, const void* K, const void* V, const void* O, const float* L,
+                    const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                    float scale, void* stream) {
     g_last_error[0] = '\0';
     if ((stages & FA2_BWD_ALL) == 0 || (stages & ~(FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC)) != 0)
         return fail(FA2_ERR_INVALID_ARGUMENT,
@@ -257,6 +284,12 @@ fa2_status bwd_impl(bool f16, unsigned stages, const void* Q, const void* K, con
                                 Hkv, N, d, scale, &empty, &sz);
     if (s != FA2_OK || empty) return s;
     const WorkspaceLayout wl = workspace_layout(sz.rows_pad, sz.q_elems);
+    if (sparse) {
+        const void* outs[4] = {dQ, dK, dV, workspace};
+        const uint64_t ob[4] = {sz.q_elems * 2, sz.kv_elems * 2, sz.kv_elems * 2, wl.total};
+        s = validate_mask(bmask, N, d, outs, ob, 4);
+        if (s != FA2_OK) return s;
+    }
     fa2::BwdParams p;
     p.Q = static_cast<const uint16_t*>(Q);
     p.K = static_cast<const uint16_t*>(K);
@@ -278,6 +311,8 @@ fa2_status bwd_impl(bool f16, unsigned stages, const void* Q, const void* K, con
     p.G = Hq / Hkv;
     p.scale = scale;
     p.c = (float)((double)scale * kLog2e);
+    p.bmask = sparse ? bmask : nullptr;
+    p.nb = (N + fa2::kSparseBlock - 1) / fa2::kSparseBlock;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = f16 ? fa2_f16::launch_bwd(p, d, causal != 0, stages, st)
                        : fa2::launch_bwd(p, d, causal != 0, stages, st);
@@ -291,19 +326,19 @@ extern "C" {
 
 fa2_status fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq,
                    int Hkv, int N, int d, int causal, float scale, void* stream) {
-    return fwd_impl(false, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+    return fwd_impl(false, false, nullptr, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
 fa2_status fa2_fwd_f16(const void* Q, const void* K, const void* V, void* O, float* L, int B,
                        int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
-    return fwd_impl(true, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+    return fwd_impl(true, false, nullptr, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
 fa2_status fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                    const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
                    float scale, void* stream) {
-    return bwd_impl(false, FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
+    return bwd_impl(false, FA2_BWD_ALL, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
                     B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
@@ -311,7 +346,7 @@ fa2_status fa2_bwd_stages(unsigned stages, const void* Q, const void* K, const v
                           const void* O, const float* L, const void* dO, void* dQ, void* dK,
                           void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
                           int Hkv, int N, int d, int causal, float scale, void* stream) {
-    return bwd_impl(false, stages, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
+    return bwd_impl(false, stages, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
                     Hkv, N, d, causal, scale, stream);
 }
 
@@ -319,7 +354,7 @@ fa2_status fa2_bwd_f16(const void* Q, const void* K, const void* V, const void* 
                        const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                        size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
                        float scale, void* stream) {
-    return bwd_impl(true, FA2_BWD_ALL, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
+    return bwd_impl(true, FA2_BWD_ALL, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes,
                     B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
@@ -327,8 +362,23 @@ fa2_status fa2_bwd_stages_f16(unsigned stages, const void* Q, const void* K, con
                               const void* O, const float* L, const void* dO, void* dQ, void* dK,
                               void* dV, void* workspace, size_t workspace_bytes, int B, int Hq,
                               int Hkv, int N, int d, int causal, float scale, void* stream) {
-    return bwd_impl(true, stages, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
+    return bwd_impl(true, stages, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
                     Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* L,
+                                const unsigned char* block_mask, int B, int Hq, int Hkv, int N,
+                                int d, int causal, float scale, void* stream) {
+    return fwd_impl(false, true, block_mask, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_block_sparse(const void* Q, const void* K, const void* V, const void* O,
+                                const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                                const unsigned char* block_mask, void* workspace,
+                                size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                int causal, float scale, void* stream) {
+    return bwd_impl(false, FA2_BWD_ALL, true, block_mask, Q, K, V, O, L, dO, dQ, dK, dV, workspace,
+                    workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
 }  // extern "C"

@@ -104,7 +104,8 @@ template <> struct BwdCfg<256> { static constexpr int BC = 64, NW = 2, BR = 32; 
 
 // ---------------------------------------------------------------------------------------------
 // bwd_pre: per padded row of each head, D_i = sum_d dO_id * O_id (fp32) and
-// L_i * log2(e); rows past N get D = 0 and +inf (so P = 0 there).  Zeroes the
+// L_i * log2(e); rows past N get D = 0 and +inf (so P = 0 there), and so do
+// rows whose L is -inf (block-sparse rows without an unmasked key).  Zeroes the
 // dQ accumulator row when dQ is accumulated with atomics.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long rows_pad, int zero_dq) {
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
     if (rp < rows_pad && part == 0) {
         p.Dneg[rp] = -acc;
-        p.L2[rp] = valid ? p.L[row] * kLog2e : kInf;
+        const float l = valid ? p.L[row] : -kInf;
+        p.L2[rp] = l != -kInf ? l * kLog2e : kInf;
     }
 }
 
@@ -742,7 +744,7 @@ void bwd_pair_kernel(const BwdParams p) {
 // drain the pipeline.  The stage loop is unrolled by eight so that every
 // buffer offset is a compile-time immediate.  The dQ^T accumulators (128
 // registers at d = 128) live in AGPRs.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_pipe_kernel(const BwdParams p) {
     constexpr int NW = 4, U = 2, BRQ = 32 * U * NW, BT = 64;
@@ -804,11 +806,43 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         dq_d[u] = q < N ? -p.Dneg[row] : 0.f;
     }
 
-    const int n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
-    const int n_t = (n_kb + 1) / 2;
+    // 32-key blocks and 64-key tiles of the walk.  Block-sparse: the list
+    // entries, the tiles of every key block that either of the workgroup's
+    // two 128-row mask blocks needs, flagged with the mask blocks that need
+    // them (as in the forward); a wave masks the tiles its own mask block
+    // does not need.
+    int n_kb, n_t;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(BRQ == 2 * kSparseBlock && 2 * BT == kSparseBlock, "two mask blocks, two tiles per block");
+        __shared__ uint16_t tl_arr[kSparseMaxN / BT];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int r0 = q0 / kSparseBlock, nb = p.nb;
+            const bool has1 = q0 + kSparseBlock < N;
+            const int n = build_tile_list(tl, nb, (N + BT - 1) / BT, lane, [&](int c) {
+                int f = 0;
+                if (p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0)) f |= 1;
+                if (has1 && p.bmask[(size_t)(r0 + 1) * nb + c] != 0 && (!CAUSAL || c <= r0 + 1)) f |= 2;
+                return f;
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_t = __builtin_amdgcn_readfirstlane(tl_count);
+        n_kb = 2 * n_t;
+    } else {
+        n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
+        n_t = (n_kb + 1) / 2;
+    }
+    auto tile_at = [&](int t) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)(tl[t] & 0xfff));
+        else return t;
+    };
 
     auto copy_part = [&](int t, int buf, int j) {
-        const int kv0 = min(t, n_t - 1) * BT;
+        const int kv0 = tile_at(min(t, n_t - 1)) * BT;
         const int last = N - 1 - kv0;
         const int i = j % PERW;
         const int R = (wave * PERW + i) * RPI;
@@ -927,8 +961,23 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
             }
         };
         {
-            const int kb0 = 32 * (s - 1);
-            if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
+            // Block s - 1 (stages past the last block compute scores nobody reads).
+            int kb0;
+            bool own = true;
+            if constexpr (SPARSE) {
+                const int bi = min(max(s - 1, 0), n_kb - 1);
+                const int e = __builtin_amdgcn_readfirstlane((int)tl[bi >> 1]);
+                kb0 = (e & 0xfff) * BT + 32 * (bi & 1);
+                own = ((e >> (12 + (wave >> 1))) & 1) != 0;
+            } else {
+                kb0 = 32 * (s - 1);
+            }
+            if (!own) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sc[P_EL][u][i] = -kInf;
+            } else if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -978,6 +1027,8 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         }
     };
 
+    // A block-sparse workgroup with no tile only writes dQ = 0.
+    if (!SPARSE || n_t > 0) {
     for (int i = tid; i < kTile / 16; i += 64 * NW) {
         lds_store16(Kbuf + 3 * kTile + 16 * i, u32x4{0, 0, 0, 0});
         lds_store16(Vbuf + 3 * kTile + 16 * i, u32x4{0, 0, 0, 0});
@@ -1000,6 +1051,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         if (s + 7 < n_stage) stage(std::integral_constant<int, 7>{}, s + 7);
     }
     wait_vm_all();
+    }
     // The accumulators were last written by matrix products issued from inline
     // assembly, which the compiler does not track: wait them out before reading.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1313,7 +1365,7 @@ void bwd_dq256_kernel(const BwdParams p) {
 // since a score accumulator register holds the 8 queries, in the order of the
 // transposed reads, that the B operand of a 16-query step needs.  Within a
 // tile, the vector work of one query block overlaps the products of the other.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_kv_kernel(const BwdParams p) {
     constexpr int NW = 4, BC = 32 * NW, BR = kBwdRowPad;
@@ -1372,11 +1424,37 @@ void bwd_kv_kernel(const BwdParams p) {
     }
 
     // Query tiles: for each of the G query heads sharing this K/V head, the
-    // 64-row tiles from the first one the causal mask lets through.
+    // 64-row tiles from the first one the causal mask lets through.  Block-
+    // sparse: the tiles of the query blocks whose mask byte in this key
+    // block's column is set (and, causal, that end at or below its first
+    // key), compacted into an LDS list by wave 0.
     const int n_qt = (N + BR - 1) / BR;
     const int i_begin = CAUSAL ? kv0 / BR : 0;
-    const int n_i = n_qt - i_begin;
+    int n_i;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(BC == kSparseBlock && 2 * BR == kSparseBlock, "one mask column, two query tiles per block");
+        __shared__ uint16_t tl_arr[kSparseMaxN / BR];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int nb = p.nb;
+            const int n = build_tile_list(tl, nb, n_qt, lane, [&](int r) {
+                return p.bmask[(size_t)r * nb + kvtile] != 0 && (!CAUSAL || r >= kvtile) ? 1 : 0;
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_i = __builtin_amdgcn_readfirstlane(tl_count);
+    } else {
+        n_i = n_qt - i_begin;
+    }
     const int n_iter = n_i * p.G;
+    // First row of query tile i of the walk.
+    auto qrow_at = [&](int i) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)(tl[i] & 0xfff)) * BR;
+        else return (i_begin + i) * BR;
+    };
 
     // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
     // tile program spreads over the slots of its last phase: Q and dO rows
@@ -1394,7 +1472,7 @@ void bwd_kv_kernel(const BwdParams p) {
     };
     auto plan_copy = [&](int it, FA2_LDS char* T) {
         const int hq = hk * p.G + it / n_i;
-        const int qt0 = (i_begin + it % n_i) * BR;
+        const int qt0 = qrow_at(it % n_i);
         const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
         const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
         TileCopy c;
@@ -1593,7 +1671,7 @@ void bwd_kv_kernel(const BwdParams p) {
     auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        tile(T, (i_begin + it % n_i) * BR, plan_copy(min(it + 2, n_iter - 1), Tw));
+        tile(T, qrow_at(it % n_i), plan_copy(min(it + 2, n_iter - 1), Tw));
         wait_vm_keep<NCOPY>();          // tile it+1, issued one step earlier, has landed
         barrier_lds();
     };
@@ -1989,6 +2067,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
     const long rows = (long)p.B * p.Hq * p.N;
     const long rows_pad = (long)p.B * p.Hq * p.Npad;
     const bool atomic_dq = (stages & 8u) != 0;
+    if (p.bmask && (D > 128 || atomic_dq)) return hipErrorInvalidValue;   // block-sparse: d <= 128, dQ pass
     if (stages & 1u) {
         constexpr int RPB = 256 / (D / 8);
         long rows_arg = rows_pad;
@@ -2008,7 +2087,8 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 fn = reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>);
                 threads = 512;
             } else {
-                fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL>);
+                fn = p.bmask ? reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, true>)
+                             : reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false>);
                 threads = 256;
             }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
@@ -2036,7 +2116,9 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
         const int rows_per_wg = D <= 128 ? 256 : 128;
         const long grid = (long)p.B * p.Hq * ((p.N + rows_per_wg - 1) / rows_per_wg);
         const void* fn;
-        if constexpr (D <= 128) fn = reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL>);
+        if constexpr (D <= 128)
+            fn = p.bmask ? reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL, true>)
+                         : reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL, false>);
         else fn = reinterpret_cast<const void*>(&bwd_dq256_kernel<CAUSAL>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, stream);
     }

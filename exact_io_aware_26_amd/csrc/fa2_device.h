@@ -140,6 +140,34 @@ __device__ __forceinline__ void level_head(int idx, int Hq, int G, int B, int& b
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block-sparse tile list, built by one wave: for the blocks c < n_blk whose
+// flags(c) (a lane's block; 0 = not needed, else a bit set of up to 3 bits)
+// are non-zero, in increasing c, the entries of its two 64-wide tiles 2c and
+// 2c + 1 as (tile | flags << 12); a block past an odd tile count holds only
+// tile 2c.  Returns the number of entries (wave-uniform).  Tile indices must
+// be below 4096.
+template <typename Flags>
+__device__ __forceinline__ int build_tile_list(FA2_LDS uint16_t* list, int n_blk, int n_tiles, int lane,
+                                               Flags flags) {
+    int count = 0;
+    bool single = false;
+    for (int c0 = 0; c0 < n_blk; c0 += 64) {
+        const int c = c0 + lane;
+        const int f = c < n_blk ? flags(c) : 0;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(f != 0);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (f != 0) {
+            const int pos = count + 2 * (int)below;
+            list[pos] = (uint16_t)((2 * c) | (f << 12));
+            if (2 * c + 1 < n_tiles) list[pos + 1] = (uint16_t)((2 * c + 1) | (f << 12));
+        }
+        single = single || __builtin_amdgcn_ballot_w64(f != 0 && 2 * c + 1 >= n_tiles) != 0;
+        count += 2 * __builtin_popcountll(m);
+    }
+    return single ? count - 1 : count;   // the single-tile block is the last entry
+}
+
 // 16-byte LDS load / store.
 __device__ __forceinline__ u32x4 lds_load16(const FA2_LDS char* p) {
     return *reinterpret_cast<const FA2_LDS u32x4*>(p);

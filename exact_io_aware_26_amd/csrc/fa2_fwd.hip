@@ -76,7 +76,7 @@ template <int D> __device__ __forceinline__ int swz(int row) {
 //     instead of 1, and the O~ rescale becomes rare.
 constexpr float kLazyMax = 8.0f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_pipe_kernel(const FwdParams p) {
     constexpr int NW = 8, ROWS = 32 * NW, BC = 64;
@@ -129,8 +129,53 @@ void fwd_pipe_kernel(const FwdParams p) {
     }
 
     // Tiles the workgroup streams, and tiles this wave computes on.
-    const int n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
-    const int n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+    //   Dense: tiles 0 .. n_kv-1 (causal: up to the workgroup's last row).
+    //   Block-sparse: the list entries 0 .. n_kv-1, the tiles of every key
+    //   block that either of the workgroup's two 128-row mask blocks needs
+    //   (its mask byte is set and, when causal, the block starts at or below
+    //   the mask block's last row), each entry flagged with the mask blocks
+    //   that need it.  A wave computes every entry up to its own causal limit
+    //   and masks the tiles its own mask block does not need, so the
+    //   score-ahead pipeline below stays the dense one.
+    int n_kv, n_w;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(ROWS == 2 * kSparseBlock && 2 * BC == kSparseBlock, "two mask blocks, two tiles per block");
+        __shared__ uint16_t tl_arr[kSparseMaxN / BC];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int r0 = q0 / kSparseBlock, nb = p.nb;
+            const bool has1 = q0 + kSparseBlock < N;
+            const int n = build_tile_list(tl, nb, (N + BC - 1) / BC, lane, [&](int c) {
+                int f = 0;
+                if (p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0)) f |= 1;
+                if (has1 && p.bmask[(size_t)(r0 + 1) * nb + c] != 0 && (!CAUSAL || c <= r0 + 1)) f |= 2;
+                return f;
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_kv = __builtin_amdgcn_readfirstlane(tl_count);
+        n_w = wq0 >= N ? 0 : n_kv;
+        if (CAUSAL) {
+            const int t_last = min(wq0 + 31, N - 1) / BC;
+            while (n_w > 0 && (tl[n_w - 1] & 0xfff) > t_last) --n_w;
+            n_w = __builtin_amdgcn_readfirstlane(n_w);
+        }
+    } else {
+        n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
+        n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+    }
+    // Key tile of step j, and (block-sparse) whether this wave's mask block needs it.
+    auto tile_at = [&](int j) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)(tl[j] & 0xfff));
+        else return j;
+    };
+    auto own_at = [&](int j) -> bool {
+        if constexpr (SPARSE) return ((__builtin_amdgcn_readfirstlane((int)tl[j]) >> (12 + (wave >> 2))) & 1) != 0;
+        else return true;
+    };
 
     // Copy tile t of K or V into LDS.  Lane i of a copy instruction writes
     // bytes 16*i.. of its 1 KiB (tile row R + i / CPR, 16-byte slot i % CPR),
@@ -183,9 +228,14 @@ void fwd_pipe_kernel(const FwdParams p) {
             }
     };
 
-    auto mask = [&](int t, f32x16 (&s)[2]) {
-        const int kv0 = t * BC;
-        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+    auto mask = [&](int j, f32x16 (&s)[2]) {
+        const int kv0 = tile_at(j) * BC;
+        if (!own_at(j)) {
+#pragma unroll
+            for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[bs][r] = kNegInf;
+        } else if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
 #pragma unroll
             for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
@@ -214,12 +264,15 @@ void fwd_pipe_kernel(const FwdParams p) {
         const float m_new = mx > m_run + kLazyMax ? mx : m_run;
         const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
         m_run = m_new;
+        // Block-sparse rows may not have seen an unmasked key yet (m = -inf):
+        // exp2(-inf - 0) = 0 then, where -inf - (-inf) would be NaN.
+        const float m_sub = SPARSE && m_new == kNegInf ? 0.f : m_new;
 #pragma unroll
         for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
-                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
+                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_sub));
+                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_sub));
                 pp[bs][r >> 1] = pack_el(s[bs][r], s[bs][r + 1]);
             }
         return alpha;
@@ -256,14 +309,16 @@ void fwd_pipe_kernel(const FwdParams p) {
         }
     };
 
+    // A block-sparse workgroup may have no tile at all: it only writes O = 0, L = -inf.
+    if (!SPARSE || n_kv > 0) {
     // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
-    copy_tile(Kh, 0, K0);
-    copy_tile(Vh, 0, V0);
+    copy_tile(Kh, tile_at(0), K0);
+    copy_tile(Vh, tile_at(0), V0);
     if (1 < n_kv) {
-        copy_tile(Kh, 1, K1);
-        copy_tile(Vh, 1, V1);
+        copy_tile(Kh, tile_at(1), K1);
+        copy_tile(Vh, tile_at(1), V1);
     }
-    if (2 < n_kv) copy_tile(Kh, 2, K2);
+    if (2 < n_kv) copy_tile(Kh, tile_at(2), K2);
     wait_vm_all();
     __syncthreads();
     f32x16 sa[2], sb[2];       // scores of the current and the next tile, alternating
@@ -278,8 +333,8 @@ void fwd_pipe_kernel(const FwdParams p) {
                     f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        copy_tile(Kh, min(j + 3, n_kv - 1), Kw);
-        copy_tile(Vh, min(j + 2, n_kv - 1), Vw);
+        copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
+        copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
         if (j < n_w) {
             mask(j, s_cur);
             uint32_t pp[2][8];
@@ -322,11 +377,13 @@ void fwd_pipe_kernel(const FwdParams p) {
         if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
     }
     wait_vm_all();
+    }
 
-    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l)
-    if (n_w > 0) {
+    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l); a block-sparse row
+    // without any unmasked key has l = 0: O = 0 and L = -inf.
+    if (SPARSE ? wq0 < N : n_w > 0) {
         const float l_tot = sum_halves(l_run);
-        const float inv = 1.0f / l_tot;
+        const float inv = SPARSE && !(l_tot > 0.f) ? 0.f : 1.0f / l_tot;
         if (q < N) {
             uint16_t* Orow = p.O + qhead + (size_t)q * D;
 #pragma unroll
@@ -339,7 +396,9 @@ void fwd_pipe_kernel(const FwdParams p) {
                     w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + d0) = w;
                 }
-            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
+            if (g == 0)
+                p.L[((size_t)b * p.Hq + hq) * N + q] =
+                    SPARSE && !(l_tot > 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
         }
     }
 }
@@ -625,9 +684,11 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     if constexpr (D <= 128) {
         arg.n_qtiles = (p.N + 255) / 256;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
-        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL>),
-                               dim3((unsigned)grid), dim3(512), args, 0, stream);
+        const void* fn = p.bmask ? reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true>)
+                                 : reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512), args, 0, stream);
     } else {
+        if (p.bmask) return hipErrorInvalidValue;   // block-sparse: d <= 128 only
         arg.n_qtiles = (p.N + 127) / 128;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
         return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe256_kernel<CAUSAL>),

@@ -5,6 +5,13 @@
 
 namespace fa2 {
 
+// Block-sparse attention: the mask has one byte per block of kSparseBlock
+// query rows x kSparseBlock keys, shared by every batch and head; the kernels
+// compact a workgroup's mask row or column into an LDS list of tile indices,
+// which bounds N.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxN = 262144;
+
 struct FwdParams {
     const uint16_t* Q;  // bf16 (f16 in fa2_f16) [B, Hq, N, D]
     const uint16_t* K;  // bf16 [B, Hkv, N, D]
@@ -14,6 +21,8 @@ struct FwdParams {
     int B, Hq, Hkv, N, G;
     int n_qtiles;       // ceil(N / rows per workgroup)
     float c;            // scale * log2(e): scores enter exp2 in the log2 domain
+    const uint8_t* bmask;  // block-sparse mask [nb, nb] (NULL: dense attention)
+    int nb;                // ceil(N / kSparseBlock)
 };
 
 struct BwdParams {
@@ -33,6 +42,8 @@ struct BwdParams {
     int Npad;      // N rounded up to a multiple of kBwdRowPad
     float scale;
     float c;       // scale * log2(e)
+    const uint8_t* bmask;  // block-sparse mask [nb, nb] (NULL: dense attention)
+    int nb;                // ceil(N / kSparseBlock)
 };
 
 // Row padding of the backward's per-row workspace arrays (one query tile of
@@ -57,6 +68,8 @@ using fa2::BwdParams;
 using fa2::FwdParams;
 using fa2::kBwdRowPad;
 using fa2::kFwdRows;
+using fa2::kSparseBlock;
+using fa2::kSparseMaxN;
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, unsigned stages, hipStream_t stream);
 }  // namespace fa2_f16

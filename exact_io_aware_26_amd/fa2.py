@@ -23,11 +23,13 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
-           "fa2_bwd_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
+           "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
            "fa2_last_error")
 DTYPES = (torch.bfloat16, torch.float16)
 
 BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
+SPARSE_BLOCK = 128            # query rows and keys per block-sparse mask block
+SPARSE_MAX_N = 262144
 
 _lib = None
 
@@ -60,6 +62,11 @@ def load(path: str | None = None):
         fn = getattr(lib, name)
         fn.argtypes = like.argtypes
         fn.restype = i
+    lib.fa2_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd_block_sparse.restype = i
+    lib.fa2_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         i, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_block_sparse.restype = i
     lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_bwd_workspace_bytes.restype = sz
     lib.fa2_validate_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
@@ -177,5 +184,83 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
              B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    _check(st, lib)
+    return dq, dk, dv
+
+
+def _block_mask(block_mask: torch.Tensor, N: int, device) -> torch.Tensor:
+    """The mask as the library reads it: contiguous bytes [nb, nb] on q's device (bool is viewed, not copied)."""
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dtype != torch.uint8:
+        raise TypeError(f"block_mask must be uint8 or bool, got {block_mask.dtype}")
+    if tuple(block_mask.shape) != (nb, nb) or not block_mask.is_contiguous():
+        raise ValueError(f"block_mask must be a contiguous [{nb}, {nb}] tensor, got {tuple(block_mask.shape)}")
+    if block_mask.device != device:
+        raise ValueError("block_mask must be on q's device")
+    return block_mask
+
+
+def forward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
+                         causal: bool = False, scale: float | None = None,
+                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Block-sparse forward (bf16): scores of 128 x 128 blocks whose mask byte is 0 are masked.
+
+    block_mask [ceil(N/128), ceil(N/128)] uint8 or bool on q's device, shared by every
+    batch and head.  Rows with no unmasked key get o = 0 and lse = -inf.
+    """
+    lib = load()
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("block-sparse attention takes bfloat16 tensors")
+    bm = _block_mask(block_mask, N, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype")
+    st = lib.fa2_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(bm),
+                                  B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    _check(st, lib)
+    return out, lse
+
+
+def backward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          lse: torch.Tensor, do: torch.Tensor, block_mask: torch.Tensor,
+                          causal: bool = False, scale: float | None = None,
+                          workspace: torch.Tensor | None = None, grads=None):
+    """Gradients of the block-sparse forward (same mask; o, lse from forward_block_sparse)."""
+    lib = load()
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("block-sparse attention takes bfloat16 tensors")
+    bm = _block_mask(block_mask, N, q.device)
+    for name, t in (("o", o), ("do", do)):
+        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped like q, in q's dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.dtype != q.dtype or t.shape != like.shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor shaped like its input, in q's dtype")
+    st = lib.fa2_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(bm), _ptr(workspace),
+                                  workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)),
+                                  float(scale), _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv

@@ -71,3 +71,37 @@ def attention_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int,
     if fmt != "bf16":
         raise ValueError(f"unknown element format {fmt!r}")
     return seeded_bf16(seed, shapes)
+
+
+SPARSE_BLOCK = 128   # query rows and keys per block-sparse mask block
+
+
+def block_mask(kind: str, N: int, seed: int = 0, density: float = 0.5, window: int = 4) -> np.ndarray:
+    """A block-sparse mask pattern, uint8 [ceil(N/128), ceil(N/128)] (row = query block).
+
+    kind: "ones", "zeros", "diagonal", "column0" (every query block sees key block 0 only),
+    "random" (each block kept with probability ``density``, PCG64 ``default_rng(seed)``),
+    "local_global" (the ``window`` key blocks ending at the query block's own, plus key
+    block 0: a sliding window with one global block), "strided" (key blocks c with
+    (r - c) % 4 == 0).
+    """
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    r = np.arange(nb)[:, None]
+    c = np.arange(nb)[None, :]
+    if kind == "ones":
+        m = np.ones((nb, nb), dtype=bool)
+    elif kind == "zeros":
+        m = np.zeros((nb, nb), dtype=bool)
+    elif kind == "diagonal":
+        m = r == c
+    elif kind == "column0":
+        m = np.broadcast_to(c == 0, (nb, nb))
+    elif kind == "random":
+        m = np.random.default_rng(seed).random((nb, nb)) < density
+    elif kind == "local_global":
+        m = ((c <= r) & (c > r - window)) | (c == 0)
+    elif kind == "strided":
+        m = (r - c) % 4 == 0
+    else:
+        raise ValueError(f"unknown block mask kind {kind!r}")
+    return np.ascontiguousarray(m, dtype=np.uint8)

@@ -202,3 +202,31 @@ def test_bwd_stage_mask(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         fa2.load(str(tmp_path / "nope.so"))
+
+
+def test_block_sparse_entry_points_check_the_mask_before_any_hip_call(lib):
+    q, k, v, o, L = (addr(i) for i in range(5))
+    mask = addr(5)
+    fwd = lib.fa2_fwd_block_sparse
+    # NULL mask with work; an empty problem needs none.
+    assert fwd(q, k, v, o, L, None, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
+    assert fwd(None, None, None, None, None, None, 2, 4, 2, 0, 128, 1, 0.1, None) == OK
+    # Head dims and sizes the block-sparse kernels do not cover.
+    assert fwd(q, k, v, o, L, mask, 2, 4, 2, 300, 256, 1, 0.1, None) == UNSUPPORTED
+    assert fwd(q, k, v, o, L, mask, 1, 1, 1, fa2.SPARSE_MAX_N + 1, 64, 1, 0.1, None) == UNSUPPORTED
+    # An output overlapping the mask (mask inside O, and inside L).
+    assert fwd(q, k, v, o, L, o + 64, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
+    assert fwd(q, k, v, o, L, L + 8, 2, 4, 2, 300, 128, 0, 0.1, None) == INVALID
+    # The dense checks still come first.
+    assert fwd(q, k, v, o, L, mask, 2, 6, 4, 300, 128, 1, 0.1, None) == INVALID
+    p = [addr(i) for i in range(9)]
+    ws = addr(9)
+    nbytes = ws_bytes(lib, 2, 4, 2, 300, 128)
+    bwd = lib.fa2_bwd_block_sparse
+    assert bwd(*p, None, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
+    assert "block_mask" in lib.fa2_last_error().decode()
+    nbytes256 = ws_bytes(lib, 2, 4, 2, 300, 256)
+    assert bwd(*p, addr(10), ws, nbytes256, 2, 4, 2, 300, 256, 1, 0.1, None) == UNSUPPORTED
+    assert bwd(*p, p[6] + 16, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID   # inside dQ
+    assert bwd(*p, ws + 512, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID    # inside the workspace
+    assert bwd(*p, addr(10), ws, nbytes - 1, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
