@@ -52,3 +52,20 @@ BWD = Workload("fwd_bwd_causal_b4_h16_n8192_d128", 4, 16, 16, 8192, 128, True, s
 
 ALL = [TINY, SHORT_NONCAUSAL, SHORT_CAUSAL, LONG, GQA_D128, GQA_D256, BWD]
 BY_NAME = {w.name: w for w in ALL}
+
+
+def block_sparse_fwd_flops(mask, B: int, Hq: int, N: int, d: int, causal: bool) -> float:
+    """Forward FLOPs of block-sparse attention in the same convention: 4 * d per
+    (query, key) pair of every kept 128 x 128 block, a block on the causal
+    diagonal counted as half its pairs (as the dense causal count halves N^2).
+    The backward is 2.5 times this."""
+    import numpy as np
+    bs = 128
+    m = np.asarray(mask) != 0
+    nb = m.shape[0]
+    size = np.minimum(bs, N - bs * np.arange(nb)).astype(np.float64)   # rows (= keys) per block
+    pairs = np.outer(size, size)
+    if causal:
+        r, c = np.indices((nb, nb))
+        pairs = np.where(c < r, pairs, np.where(c == r, pairs / 2.0, 0.0))
+    return 4.0 * B * Hq * d * float(np.sum(pairs[m]))
