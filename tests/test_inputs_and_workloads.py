@@ -61,3 +61,24 @@ def test_f16_inputs_are_the_same_draws_rounded_to_binary16():
         pass
     else:
         raise AssertionError("an unknown element format must be rejected")
+
+
+def test_block_sparse_flops_and_masks():
+    from exact_io_aware_26_amd import inputs, workloads
+    # All kept: the dense count (N a multiple of the block).
+    for causal in (False, True):
+        w = workloads.Workload("x", 2, 4, 2, 1024, 64, causal, seed=0)
+        m = inputs.block_mask("ones", 1024)
+        assert workloads.block_sparse_fwd_flops(m, 2, 4, 1024, 64, causal) == w.fwd_flops()
+    # Diagonal blocks of N = 300 (sizes 128, 128, 44), by hand.
+    m = inputs.block_mask("diagonal", 300)
+    assert m.shape == (3, 3) and m.sum() == 3
+    pairs = 128 * 128 + 128 * 128 + 44 * 44
+    assert workloads.block_sparse_fwd_flops(m, 1, 1, 300, 64, False) == 4 * 64 * pairs
+    assert workloads.block_sparse_fwd_flops(m, 1, 1, 300, 64, True) == 4 * 64 * pairs / 2
+    # Patterns.
+    lg = inputs.block_mask("local_global", 1000, window=4)
+    assert lg[7].tolist() == [1, 0, 0, 0, 1, 1, 1, 1] and lg[0].tolist() == [1] + [0] * 7
+    assert inputs.block_mask("zeros", 129).sum() == 0
+    r1, r2 = inputs.block_mask("random", 2000, seed=3), inputs.block_mask("random", 2000, seed=3)
+    assert (r1 == r2).all() and 0 < r1.sum() < r1.size
