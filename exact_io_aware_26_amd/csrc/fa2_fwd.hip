@@ -535,60 +535,6 @@ void fwd_pipe256_kernel(const FwdParams p) {
     float m_run = kNegInf;   // reference max of c * S (log2 domain), equal in lanes l and l ^ 32
     float l_run = 0.f;       // this lane's half of the row sum, relative to m_run
 
-    // P = exp2(c S - m) in place (fp32, for the row sum) and packed to bf16
-    // (the B operand of the P V product); returns the rescale factor of O~ and l.
-    auto softmax = [&](f32x16 (&s)[NBS], uint32_t (&pp)[NBS][8]) -> float {
-        float mx = kNegInf;
-#pragma unroll
-        for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
-        mx = max_halves(mx) * p.c;
-        const float m_new = mx > m_run + kLazyMax ? mx : m_run;
-        const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
-        m_run = m_new;
-#pragma unroll
-        for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_new));
-                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_new));
-                pp[bs][r >> 1] = pack_el(s[bs][r], s[bs][r + 1]);
-            }
-        return alpha;
-    };
-
-    auto row_sum = [&](const f32x16 (&pr)[NBS], float alpha) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) lsum += pr[bs][r] + pr[bs][r + 1];
-        l_run = fmaf(l_run, alpha, lsum);
-    };
-
-    // O^T += V^T P^T: V^T fragments by transposed reads of the row-major V tile
-    // (rows 16*kk + 4*g + j16/4 and +8, columns 32*db + 16*half + 4*(j16 % 4)).
-    auto pv = [&](const FA2_LDS char* Vs, const uint32_t (&pp)[NBS][8]) {
-        const int j16 = lane & 15;
-        const int x = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);    // chunk within a 32-column block
-        const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
-        int vb1 = r1 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r1));
-        int vb2 = r2 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r2));
-        asm volatile("" : "+v"(vb1), "+v"(vb2));
-#pragma unroll
-        for (int kk = 0; kk < 2 * NBS; ++kk) {
-            const int bs = kk >> 1, h = kk & 1;
-            const el8 bfrag = as_el8(u32x4{pp[bs][4 * h], pp[bs][4 * h + 1], pp[bs][4 * h + 2], pp[bs][4 * h + 3]});
-#pragma unroll
-            for (int db = 0; db < NBD; ++db) {
-                const s16x4 t1 = lds_load_tr(Vs + 16 * kk * RB + (vb1 ^ (64 * db)));
-                const s16x4 t2 = lds_load_tr(Vs + 16 * kk * RB + (vb2 ^ (64 * db)));
-                o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
-            }
-        }
-    };
-
     // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
     copy_tile(Kh, 0, K0);
     copy_tile(Vh, 0, V0);
@@ -603,6 +549,98 @@ void fwd_pipe256_kernel(const FwdParams p) {
     scores(K0, sa);
     __syncthreads();          // K_0 is overwritten by K_3 in step 0
 
+    // A step as two fixed slot programs, one matrix product per slot (with
+    // one wave per SIMD the issue order is the overlap).  Phase 1 issues the
+    // 16 products of S_{j+1}, each K operand read kPf slots ahead, and spreads
+    // the softmax of S_j over the slots: the row max in slots 0-3, the new
+    // reference max in slot 4, two exponentials and one packing per slot in
+    // slots 5-12, and the first V^T reads of phase 2 in slots 12-15.  Phase 2
+    // issues the 16 P V products with their operands read kPf slots ahead and
+    // one row-sum addition per slot.  A scheduling fence between slots keeps
+    // this order; an empty asm that redefines each staged value keeps the
+    // compiler from sinking it to its first use.
+    constexpr int kPf = 4;
+    static_assert(NBS == 1 && KSD == 16 && 2 * NBD == 16, "slot programs for d = 256, 32-key tiles");
+    auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+    int pvb1 = 0, pvb2 = 0;
+    auto v_bases = [&]() {
+        const int j16 = lane & 15;
+        const int x = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);    // chunk within a 32-column block
+        const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
+        pvb1 = r1 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r1));
+        pvb2 = r2 * RB + 8 * (j16 & 1) + 16 * (x ^ swz<D>(r2));
+        asm volatile("" : "+v"(pvb1), "+v"(pvb2));
+    };
+    // V^T fragment of P V product k (keys 16 (k / 8) .., head-dim block k % 8).
+    auto load_vt = [&](const FA2_LDS char* Vs, int k, s16x4 (&t)[2]) {
+        const int kk = k / NBD, db = k % NBD;
+        t[0] = lds_load_tr(Vs + 16 * kk * RB + (pvb1 ^ (64 * db)));
+        t[1] = lds_load_tr(Vs + 16 * kk * RB + (pvb2 ^ (64 * db)));
+    };
+    auto phase1 = [&](const FA2_LDS char* Ks, const FA2_LDS char* Vs, f32x16& sc, f32x16& sn, uint32_t (&pp)[8],
+                      s16x4 (&vt)[kPf][2]) -> float {
+        int kb = li * RB + 16 * (g ^ swz<D>(li));
+        asm volatile("" : "+v"(kb));
+        v_bases();
+        u32x4 ka[kPf];
+#pragma unroll
+        for (int k = 0; k < kPf; ++k) ka[k] = lds_load16(Ks + (kb ^ (32 * k)));
+        sn = zero16();
+        float m0 = kNegInf, m1 = kNegInf, m_sub = 0.f, alpha = 1.f;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 a = ka[ks % kPf];
+            if (ks + kPf < KSD) ka[ks % kPf] = lds_load16(Ks + (kb ^ (32 * (ks + kPf))));
+            sn = mfma32(as_el8(a), qf[ks], sn);
+            if (ks < 4) {
+                m0 = fmaxf(fmaxf(m0, sc[4 * ks]), sc[4 * ks + 1]);
+                m1 = fmaxf(fmaxf(m1, sc[4 * ks + 2]), sc[4 * ks + 3]);
+                pin(m0);
+                pin(m1);
+            } else if (ks == 4) {
+                const float mx = max_halves(fmaxf(m0, m1)) * p.c;
+                const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+                alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
+                m_run = m_new;
+                m_sub = m_new;
+                pin(m_sub);
+                pin(alpha);
+            } else if (ks < 13) {
+                const int r = 2 * (ks - 5);
+                float e0 = exp2_fast(fmaf(sc[r], p.c, -m_sub));
+                float e1 = exp2_fast(fmaf(sc[r + 1], p.c, -m_sub));
+                pin(e0);
+                pin(e1);
+                uint32_t w = pack_el(e0, e1);
+                asm volatile("" : "+v"(w));
+                pp[r >> 1] = w;
+                sc[r] = e0;
+                sc[r + 1] = e1;
+            }
+            if (ks >= KSD - kPf) load_vt(Vs, ks - (KSD - kPf), vt[ks - (KSD - kPf)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return alpha;
+    };
+    auto phase2 = [&](const FA2_LDS char* Vs, const uint32_t (&pp)[8], const f32x16& pr, s16x4 (&vt)[kPf][2],
+                      float alpha) {
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2 * NBD; ++k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int kk = k / NBD, db = k % NBD;
+            const s16x4 t1 = vt[k % kPf][0], t2 = vt[k % kPf][1];
+            if (k + kPf < 2 * NBD) load_vt(Vs, k + kPf, vt[k % kPf]);
+            const el8 bfrag = as_el8(u32x4{pp[4 * kk], pp[4 * kk + 1], pp[4 * kk + 2], pp[4 * kk + 3]});
+            o[db] = mfma32(cat_tr(t1, t2), bfrag, o[db]);
+            if (k & 1) ls1 += pr[k];
+            else ls0 += pr[k];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        l_run = fmaf(l_run, alpha, ls0 + ls1);
+    };
+
     // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
     // then P_j V_j.  Past a wave's last tile the step only copies; S_{j+1} of a
     // tile the wave does not visit is computed from whatever its buffer holds
@@ -615,28 +653,16 @@ void fwd_pipe256_kernel(const FwdParams p) {
         copy_tile(Vh, min(j + 2, n_kv - 1), Vw);
         if (j < n_w) {
             mask(j, s_cur);
-            uint32_t pp[NBS][8];
-            // Raised priority while this wave interleaves S_{j+1} with the
-            // softmax of S_j, normal for the P V products: the other wave on the
-            // SIMD then fills the matrix unit's idle slots of the mixed phase.
-            __builtin_amdgcn_s_setprio(1);
-            scores(Ks, s_next);
-            const float alpha = softmax(s_cur, pp);
-            // Materialize P here, beside the S_{j+1} products, rather than
-            // letting the compiler sink the exponentials below the branch.
-#pragma unroll
-            for (int bs = 0; bs < NBS; ++bs)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
+            uint32_t pp[8];
+            s16x4 vt[kPf][2];
+            const float alpha = phase1(Ks, Vs, s_cur[0], s_next[0], pp, vt);
             if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
                 for (int i = 0; i < NBD; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
             }
-            __builtin_amdgcn_s_setprio(0);
-            pv(Vs, pp);
-            row_sum(s_cur, alpha);
+            phase2(Vs, pp, s_cur[0], vt, alpha);
         }
         wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
         barrier_lds();
