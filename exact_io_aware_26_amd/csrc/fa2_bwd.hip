@@ -979,12 +979,14 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
                     for (int i = 0; i < 16; ++i) sc[P_EL][u][i] = -kInf;
             } else if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                for (int u = 0; u < U; ++u) {
+                    // Element i holds key kb0 + 4g + 8 (i / 4) + i % 4: masked when
+                    // that constant offset exceeds lim (one compare, one select).
+                    const int lim = (CAUSAL ? min(qu[u], N - 1) : N - 1) - kb0 - 4 * g;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                        if ((CAUSAL && key > qu[u]) || key >= N) sc[P_EL][u][i] = -kInf;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        sc[P_EL][u][i] = 8 * (i >> 2) + (i & 3) > lim ? -kInf : sc[P_EL][u][i];
+                }
             }
         }
         const bool copy_stage = (S8 & 1) == 0;
@@ -1268,12 +1270,14 @@ void bwd_dq256_kernel(const BwdParams p) {
             const int kb0 = 32 * (s - 1);
             if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                for (int u = 0; u < U; ++u) {
+                    // Element i holds key kb0 + 4g + 8 (i / 4) + i % 4: masked when
+                    // that constant offset exceeds lim (one compare, one select).
+                    const int lim = (CAUSAL ? min(qu[u], N - 1) : N - 1) - kb0 - 4 * g;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                        if ((CAUSAL && key > qu[u]) || key >= N) sc[P_EL][u][i] = -kInf;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        sc[P_EL][u][i] = 8 * (i >> 2) + (i & 3) > lim ? -kInf : sc[P_EL][u][i];
+                }
             }
         }
         // Each stage copies the next tile into the buffer that the barrier

@@ -236,13 +236,15 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[bs][r] = kNegInf;
         } else if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+            // Element (bs, r) holds key kv0 + 4g + off with off a constant; it
+            // is masked when the key exceeds min(q, N - 1) (causal) or N - 1,
+            // i.e. when off > lim: one compare and one select per element.
+            const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - kv0 - 4 * g;
 #pragma unroll
             for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
-                }
+                for (int r = 0; r < 16; ++r)
+                    s[bs][r] = 32 * bs + 8 * (r >> 2) + (r & 3) > lim ? kNegInf : s[bs][r];
         }
     };
 
@@ -519,13 +521,13 @@ void fwd_pipe256_kernel(const FwdParams p) {
     auto mask = [&](int t, f32x16 (&s)[NBS]) {
         const int kv0 = t * BC;
         if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+            // As in fwd_pipe_kernel: masked when the constant key offset exceeds lim.
+            const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - kv0 - 4 * g;
 #pragma unroll
             for (int bs = 0; bs < NBS; ++bs)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kv = kv0 + 32 * bs + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((CAUSAL && kv > q) || kv >= N) s[bs][r] = kNegInf;
-                }
+                for (int r = 0; r < 16; ++r)
+                    s[bs][r] = 32 * bs + 8 * (r >> 2) + (r & 3) > lim ? kNegInf : s[bs][r];
         }
     };
 
