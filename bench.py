@@ -189,7 +189,7 @@ def main() -> int:
                          "stage once; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path, so --gpus {args.gpus} "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path, so --gpus {args.gpus} "
               "is not supported; run with --gpus 1", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
