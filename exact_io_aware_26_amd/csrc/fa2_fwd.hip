@@ -405,10 +405,11 @@ void fwd_pipe_kernel(const FwdParams p) {
     }
 }
 
-// The pipelined forward at d = 256: the same program as fwd_pipe_kernel with
+// The pipelined forward at d = 256: the tile pipeline of fwd_pipe_kernel with
 // 32-key K/V tiles (16 KiB each, three deep per tensor), one score block per
 // step, and 4 waves (one per SIMD, 128 rows per workgroup: the O~ accumulator
-// alone takes 128 registers).
+// alone takes 128 registers).  With one wave per SIMD nothing else hides a
+// wave's latencies, so each step is issued as fixed slot programs (below).
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_pipe256_kernel(const FwdParams p) {
