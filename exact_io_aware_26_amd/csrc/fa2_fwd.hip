@@ -39,6 +39,8 @@
 #include "fa2_device.h"
 #include "fa2_kernels.h"
 
+#include <type_traits>
+
 namespace FA2_NS {
 
 namespace {
@@ -88,8 +90,12 @@ void fwd_pipe_kernel(const FwdParams p) {
     constexpr int CPR = RB / 16;         // 16-byte chunks per row
     constexpr int PERW = kTile / 1024 / NW;
     static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
-    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile];
-    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile];
+    // At d = 64 the two waves of a SIMD run half a step apart (see the loop
+    // below), which needs a fourth V buffer; K gets one too for a period-4 ring.
+    constexpr bool kPingPong = D == 64;
+    constexpr int kTile3 = kPingPong ? kTile : 16;
+    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile], Kb3[kTile3];
+    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile], Vb3[kTile3];
     FA2_LDS char* const K0 = (FA2_LDS char*)Kb0;
     FA2_LDS char* const K1 = (FA2_LDS char*)Kb1;
     FA2_LDS char* const K2 = (FA2_LDS char*)Kb2;
@@ -327,6 +333,7 @@ void fwd_pipe_kernel(const FwdParams p) {
     scores(K0, sa);
     __syncthreads();          // K_0 is overwritten by K_3 in step 0
 
+    if constexpr (!kPingPong) {
     // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
     // then P_j V_j.  Past a wave's last tile the step only copies; S_{j+1} of a
     // tile the wave does not visit is computed from whatever its buffer holds
@@ -377,6 +384,82 @@ void fwd_pipe_kernel(const FwdParams p) {
         if (j + 3 < n_kv) step(j + 3, K1, V0, K0, V2, sb, sa);
         if (j + 4 < n_kv) step(j + 4, K2, V1, K1, V0, sa, sb);
         if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
+    }
+    } else {
+    // Waves w and w + 4 share a SIMD.  Waves 0-3 run each step as (S_{j+1}
+    // with the softmax of S_j, then P_j V_j), waves 4-7 half a step later as
+    // (P_{j-1} V_{j-1}, then S_{j+1} with the softmax of S_j): while one wave
+    // of a SIMD does its vector-heavy half the other issues matrix products.
+    // This pays at d = 64, where the vector work per product is twice that of
+    // d = 128 (at d = 128 the extra live registers cost more than it gains).
+    // K and V tiles live in four-buffer rings (tile t in buffer t % 4): step j
+    // reads K_{j+1}, V_j and V_{j-1}, and copies K_{j+3} and V_{j+2} into the
+    // buffers of K_{j-1} and V_{j-2}, which no wave reads after step j - 1.
+    FA2_LDS char* const K3 = (FA2_LDS char*)Kb3;
+    FA2_LDS char* const V3 = (FA2_LDS char*)Vb3;
+    const bool late = wave >= 4;
+    uint32_t pp[2][8];         // P_j packed to bf16 (the late waves keep it for the next step)
+    auto softmax_phase = [&](int j, const FA2_LDS char* Ks, f32x16 (&s_cur)[2], f32x16 (&s_next)[2])
+        __attribute__((always_inline)) -> float {
+        mask(j, s_cur);
+        __builtin_amdgcn_s_setprio(1);
+        scores(Ks, s_next);
+        const float alpha = softmax(s_cur, pp);
+#pragma unroll
+        for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int i = 0; i < NBD; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        }
+        __builtin_amdgcn_s_setprio(0);
+        return alpha;
+    };
+    // The loop is instantiated once per wave group (LATE = the late waves), so
+    // each group's registers are allocated for its own program.
+    auto run = [&](auto late_tag) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(late_tag)::value;
+        auto step = [&](int j, const FA2_LDS char* Ks, const FA2_LDS char* Vs, const FA2_LDS char* Vp,
+                        FA2_LDS char* Kw, FA2_LDS char* Vw, f32x16 (&s_cur)[2], f32x16 (&s_next)[2])
+            __attribute__((always_inline)) {
+            copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
+            copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
+            if constexpr (!LATE) {
+                if (j < n_w) {
+                    const float alpha = softmax_phase(j, Ks, s_cur, s_next);
+                    pv(Vs, pp);
+                    row_sum(s_cur, alpha);
+                }
+            } else {
+                if (j >= 1 && j - 1 < n_w) pv(Vp, pp);
+                if (j < n_w) {
+                    const float alpha = softmax_phase(j, Ks, s_cur, s_next);
+                    row_sum(s_cur, alpha);
+                }
+            }
+            wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
+            barrier_lds();
+        };
+        for (int j = 0; j < n_kv; j += 4) {
+            step(j, K1, V0, V3, K3, V2, sa, sb);
+            if (j + 1 < n_kv) step(j + 1, K2, V1, V0, K0, V3, sb, sa);
+            if (j + 2 < n_kv) step(j + 2, K3, V2, V1, K1, V0, sa, sb);
+            if (j + 3 < n_kv) step(j + 3, K0, V3, V2, K2, V1, sb, sa);
+        }
+        // The late waves' last P V product: V_{n_kv-1} is in buffer
+        // (n_kv-1) % 4 (later copies went to other buffers).
+        if constexpr (LATE) {
+            if (n_w == n_kv) {
+                const int t = (n_kv - 1) & 3;
+                pv(t == 0 ? V0 : t == 1 ? V1 : t == 2 ? V2 : V3, pp);
+            }
+        }
+    };
+    if (late) run(std::true_type{});
+    else run(std::false_type{});
     }
     wait_vm_all();
     }
