@@ -345,29 +345,35 @@ void fwd_pipe_kernel(const FwdParams p) {
         copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
         copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
         if (j < n_w) {
-            mask(j, s_cur);
+            // Block-sparse: a tile this wave's mask block does not need gets
+            // only the products S_{j+1} (they keep the pipeline's shape).
+            const bool own = !SPARSE || own_at(j);
+            if (own) mask(j, s_cur);
             uint32_t pp[2][8];
             // Raised priority while this wave interleaves S_{j+1} with the
             // softmax of S_j, normal for the P V products: the other wave on the
             // SIMD then fills the matrix unit's idle slots of the mixed phase.
             __builtin_amdgcn_s_setprio(1);
             scores(Ks, s_next);
-            const float alpha = softmax(s_cur, pp);
-            // Materialize P here, beside the S_{j+1} products, rather than
-            // letting the compiler sink the exponentials below the branch.
+            if (own) {
+                const float alpha = softmax(s_cur, pp);
+                // Materialize P here, beside the S_{j+1} products, rather than
+                // letting the compiler sink the exponentials below the branch.
 #pragma unroll
-            for (int bs = 0; bs < 2; ++bs)
+                for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
-                for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+                    for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-                for (int i = 0; i < NBD; ++i)
+                    for (int i = 0; i < NBD; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+                        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+                }
+                if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
+                pv(Vs, pp);
+                row_sum(s_cur, alpha);
             }
-            __builtin_amdgcn_s_setprio(0);
-            pv(Vs, pp);
-            row_sum(s_cur, alpha);
+            if constexpr (SPARSE) __builtin_amdgcn_s_setprio(0);
         }
         wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
         barrier_lds();
@@ -399,6 +405,10 @@ void fwd_pipe_kernel(const FwdParams p) {
     FA2_LDS char* const V3 = (FA2_LDS char*)Vb3;
     const bool late = wave >= 4;
     uint32_t pp[2][8];         // P_j packed to bf16 (the late waves keep it for the next step)
+    // S_{j+1} beside the softmax of S_j.  (Block-sparse tiles this wave's
+    // mask block does not need are masked to -inf here rather than skipped:
+    // a branch between the products and the softmax costs this kernel more
+    // than the skipped work saves.)
     auto softmax_phase = [&](int j, const FA2_LDS char* Ks, f32x16 (&s_cur)[2], f32x16 (&s_next)[2])
         __attribute__((always_inline)) -> float {
         mask(j, s_cur);
