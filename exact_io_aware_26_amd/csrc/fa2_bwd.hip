@@ -747,7 +747,9 @@ void bwd_pair_kernel(const BwdParams p) {
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_pipe_kernel(const BwdParams p) {
-    constexpr int NW = 4, U = 2, BRQ = 32 * U * NW, BT = 64;
+    // Block-sparse: one query block per wave, so a workgroup (128 rows) is
+    // one mask row and computes no tile that its rows do not need.
+    constexpr int NW = 4, U = SPARSE ? 1 : 2, BRQ = 32 * U * NW, BT = 64;
     constexpr int RB = 2 * D;
     constexpr int kTile = BT * RB;
     constexpr int KSD = D / 16, NBD = D / 32;
@@ -807,25 +809,19 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
     }
 
     // 32-key blocks and 64-key tiles of the walk.  Block-sparse: the list
-    // entries, the tiles of every key block that either of the workgroup's
-    // two 128-row mask blocks needs, flagged with the mask blocks that need
-    // them (as in the forward); a wave masks the tiles its own mask block
-    // does not need.
+    // entries, the tiles of every key block that the workgroup's 128-row
+    // mask block needs (causal: at or below its diagonal).
     int n_kb, n_t;
     FA2_LDS uint16_t* tl = nullptr;
     if constexpr (SPARSE) {
-        static_assert(BRQ == 2 * kSparseBlock && 2 * BT == kSparseBlock, "two mask blocks, two tiles per block");
+        static_assert(BRQ == kSparseBlock && 2 * BT == kSparseBlock, "one mask block, two tiles per block");
         __shared__ uint16_t tl_arr[kSparseMaxN / BT];
         __shared__ int tl_count;
         tl = (FA2_LDS uint16_t*)tl_arr;
         if (wave == 0) {
             const int r0 = q0 / kSparseBlock, nb = p.nb;
-            const bool has1 = q0 + kSparseBlock < N;
             const int n = build_tile_list(tl, nb, (N + BT - 1) / BT, lane, [&](int c) {
-                int f = 0;
-                if (p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0)) f |= 1;
-                if (has1 && p.bmask[(size_t)(r0 + 1) * nb + c] != 0 && (!CAUSAL || c <= r0 + 1)) f |= 2;
-                return f;
+                return p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0) ? 1 : 0;
             });
             if (lane == 0) tl_count = n;
         }
@@ -963,12 +959,11 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         {
             // Block s - 1 (stages past the last block compute scores nobody reads).
             int kb0;
-            bool own = true;
+            const bool own = true;     // every list entry is needed by the workgroup's rows
             if constexpr (SPARSE) {
                 const int bi = min(max(s - 1, 0), n_kb - 1);
                 const int e = __builtin_amdgcn_readfirstlane((int)tl[bi >> 1]);
                 kb0 = (e & 0xfff) * BT + 32 * (bi & 1);
-                own = ((e >> (12 + (wave >> 1))) & 1) != 0;
             } else {
                 kb0 = 32 * (s - 1);
             }
@@ -2117,7 +2112,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                                    dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
         }
         void* args[] = {&arg};
-        const int rows_per_wg = D <= 128 ? 256 : 128;
+        const int rows_per_wg = D <= 128 && !p.bmask ? 256 : 128;   // block-sparse: one mask row
         const long grid = (long)p.B * p.Hq * ((p.N + rows_per_wg - 1) / rows_per_wg);
         const void* fn;
         if constexpr (D <= 128)
