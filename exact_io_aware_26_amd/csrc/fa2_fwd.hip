@@ -61,17 +61,19 @@ template <int D> __device__ __forceinline__ int swz(int row) {
 // rows (two waves per SIMD), so each K/V tile brought into LDS serves twice
 // as many rows as a 4-wave workgroup would.
 //   * K/V tiles are copied from global memory straight into LDS
-//     (global_load_lds_dwordx4, no staging registers), three buffers deep, K
-//     one tile ahead of V: during step j the waves read K_{j+1} and V_j while
-//     K_{j+3} and V_{j+2} are in flight.  The six buffers are distinct LDS
-//     objects and the loop is unrolled by three, so no read names the buffer
-//     being filled and the compiler adds no wait on in-flight tiles; each step
-//     waits only for the copies issued one step earlier.
+//     (global_load_lds_dwordx4, no staging registers), K one tile ahead of V:
+//     during step j the waves read K_{j+1} and V_j while K_{j+3} and V_{j+2}
+//     are in flight.  The buffers (three per tensor at d = 128, four at
+//     d = 64) are distinct LDS objects and the loop is unrolled by the ring
+//     period, so no read names the buffer being filled and the compiler adds
+//     no wait on in-flight tiles; each step waits only for the copies issued
+//     one step earlier.
 //   * Within a wave the work is software-pipelined.  Step j runs the softmax
 //     of S_j (computed one step earlier) while the matrix cores compute
 //     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j while the row sums of
 //     P_j are added up, so vector and matrix work of neighbouring tiles
-//     overlap.
+//     overlap.  At d = 64 the second wave of each SIMD runs its steps half a
+//     step later (see the loop).
 //   * The running max m is raised only when a row's new max exceeds it by more
 //     than kLazyMax (log2 units).  O~, l and L all use the same m, so this is
 //     the same algebra as the method's rescale; it only bounds P by 2^kLazyMax
