@@ -19,9 +19,10 @@
 //   bwd_kv           d = 64, 128: one workgroup per 128 keys; dK and dV stay in
 //                    registers over all query tiles (and all query heads of a
 //                    GQA group).
-//   bwd_dq_pipe      d = 64, 128: one workgroup per 256 query rows; dQ stays in
-//                    registers over all key blocks, recomputing S and dP, so no
-//                    atomics are needed and dQ is deterministic.
+//   bwd_dq_pipe      d = 64, 128: one workgroup per 256 query rows (128 with a
+//                    block mask: one mask row); dQ stays in registers over all
+//                    key blocks, recomputing S and dP, so no atomics are needed
+//                    and dQ is deterministic.
 //   bwd_kv256        d = 256: the K/V loop split over the head dim (two
 //                    workgroups per 128-key tile, 128 columns of dK, dV each).
 //   bwd_dq256        d = 256: the dQ pass with 32-key tiles.
@@ -725,7 +726,8 @@ void bwd_pair_kernel(const BwdParams p) {
 // bwd_dq_pipe: the dQ pass for d = 64 and 128.
 //
 // One workgroup = 4 wave64s, one wave per SIMD; each wave owns two 32-row query
-// blocks (u = 0, 1; 256 rows per workgroup).  Q and dO of its rows are MFMA B
+// blocks (u = 0, 1; 256 rows per workgroup; with a block mask one block, so
+// that a 128-row workgroup is one mask row).  Q and dO of its rows are MFMA B
 // operands in registers and its dQ^T accumulators stay in registers, all
 // transposed so that each lane owns one query row of each block:
 //     s  = K Q^T,  dp = V dO^T          (A: K / V rows from LDS)
