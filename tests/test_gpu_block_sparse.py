@@ -142,3 +142,27 @@ def test_block_sparse_large_sampled_rows():
     # Gradients of one head in full at N = 2048 (the oracle's backward is quadratic per head).
     check_case(6, 1, 1, 1, 2048, 128, True, "local_global")
     del fa2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_sparse_maximum_n(d):
+    """N = 262144 (the largest block-sparse N: 4096 tiles of 64 keys, the top of
+    the tile lists' 12-bit index) with a local + global mask: sampled rows of O
+    and L against the oracle, including rows of the last block; every
+    gradient element written and finite."""
+    from exact_io_aware_26_amd import fa2
+    B, Hq, Hkv, N = 1, 1, 1, fa2.SPARSE_MAX_N
+    mask = inputs.block_mask("local_global", N)
+    log(f"[sparse] maximum N={N} d={d} causal local_global ({int(mask.sum())} blocks)")
+    qb, kb, vb, dob = inputs.attention_inputs(9, B, Hq, Hkv, N, d, with_grad=True)
+    o, L, dq, dk, dv = run(qb, kb, vb, dob, mask, True)
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), f"{name} has unwritten or non-finite elements"
+    rng = np.random.default_rng(4)
+    rows = [(0, 0, 0), (0, 0, N - 1), (0, 0, N - 129), (0, 0, 131071)]
+    rows += [(0, 0, int(rng.integers(N))) for _ in range(12)]
+    rows = np.array(rows)
+    q64, k64, v64 = (inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    ro, rL = orc.forward_rows(q64, k64, v64, rows, True, 1.0 / math.sqrt(d), block_mask=mask)
+    parity.check_bf16("O rows", parity.bf16_to_f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]], ro)
+    parity.check_lse("L rows", parity.f32_to_f64(L)[rows[:, 0], rows[:, 1], rows[:, 2]], rL)
