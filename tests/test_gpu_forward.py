@@ -194,3 +194,23 @@ def test_fwd_large_scores_stay_finite():
         parity.check_bf16("O (large scores)", parity.bf16_to_f64(o), ro)
         parity.check_lse("L (large scores)", parity.f32_to_f64(L), rL,
                          atol=max(1e-3, 2e-7 * np.abs(rL).max()))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_long_sequence_sampled_rows(d, causal):
+    """N = 65536 (four times the longest benchmark sequence), GQA 2:1: sampled
+    rows, including the first and last rows of the sequence, against the oracle."""
+    B, Hq, Hkv, N = 1, 2, 1, 65536
+    log(f"[fwd] long sequence B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    qb, kb, vb = inputs.attention_inputs(11, B, Hq, Hkv, N, d)
+    o, L = run_fwd(qb, kb, vb, causal)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(L).all())
+    rows = np.array([(0, 0, 0), (0, 1, N - 1), (0, 0, N // 2), (0, 1, 255), (0, 1, 256)]
+                    + [(0, int(h), int(i)) for h, i in zip(np.random.default_rng(d).integers(Hq, size=11),
+                                                         np.random.default_rng(d + 1).integers(N, size=11))])
+    q64, k64, v64 = (inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    ro, rL = orc.forward_rows(q64, k64, v64, rows, causal, 1.0 / math.sqrt(d))
+    idx = torch.from_numpy(rows.astype(np.int64)).to(o.device)
+    parity.check_bf16("O rows", parity.bf16_to_f64(o[idx[:, 0], idx[:, 1], idx[:, 2]]), ro)
+    parity.check_lse("L rows", parity.f32_to_f64(L)[rows[:, 0], rows[:, 1], rows[:, 2]], rL)
