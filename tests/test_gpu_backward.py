@@ -204,3 +204,9 @@ def test_bwd_stages_in_separate_calls_equal_one_call(mode):
     if mode == 0:
         assert torch.equal(dq1.view(torch.int16), grads[0].view(torch.int16))
     parity.check_bf16("dQ staged", parity.bf16_to_f64(grads[0]), parity.bf16_to_f64(dq1))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_long_sequence_head(d):
+    """One head at N = 16384 (twice the benchmark sequence), causal, in full."""
+    full_case(12, 1, 1, 1, 16384, d, True)
