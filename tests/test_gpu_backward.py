@@ -210,3 +210,27 @@ def test_bwd_stages_in_separate_calls_equal_one_call(mode):
 def test_bwd_long_sequence_head(d):
     """One head at N = 16384 (twice the benchmark sequence), causal, in full."""
     full_case(12, 1, 1, 1, 16384, d, True)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("mult", [0.1, 0.5, 1.5])
+def test_fwd_bwd_caller_scale(d, mult):
+    """A caller-chosen scale, mult / sqrt(d) (score spread mult times the default's):
+    forward and backward against the oracle.
+
+    D_i = dO_i . O_i takes O from its bf16 store, and the kernel's fp32 O and the
+    oracle's O can round to neighbouring bf16 values; each such element moves D_i
+    by |dO| * ulp(O), and dQ_i, dK_j by scale * P_ij * dD_i * |K_j| (|Q_i|).  The
+    sharper the softmax, the larger P_ij at the dominant key: at twice the default
+    spread (d = 64, these inputs) dQ's worst element misses 1e-2 by 0.0025, and at
+    scale 1 (spread 8) dK's worst error is 0.15 where the oracle's working-precision
+    one is 0.09; with D taken from the kernel's own O, an fp64 re-computation lands
+    within 0.03 of the kernel's dK.  Element gates at such
+    spreads measure O's last-bit rounding, so the cases here stay at or below 1.5.
+    """
+    from tests import test_gpu_forward as tf
+    scale = mult / math.sqrt(d)
+    tf.full_case(13, 1, 2, 1, 200, d, True, scale=scale)
+    tf.full_case(14, 1, 2, 2, 130, d, False, scale=scale)
+    full_case(13, 1, 2, 1, 200, d, True, scale=scale)
+    full_case(14, 1, 2, 2, 130, d, False, scale=scale)
