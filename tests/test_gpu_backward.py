@@ -118,6 +118,16 @@ def test_bwd_gqa_full_size_head():
     head_case(w, [(1, 3)])
 
 
+@pytest.mark.parametrize("w", [workloads.SHORT_NONCAUSAL, workloads.SHORT_CAUSAL, workloads.GQA_D256],
+                         ids=lambda w: w.name)
+def test_bwd_other_workloads_full_size(w):
+    """The backward at the other full-size shapes the benchmark times (B8 H16 N2048 d64,
+    both masks; B4 Hq32 Hkv8 N4096 d256 causal): every element written and finite,
+    two K/V heads (one at d = 256, with its 4 query heads) against the oracle."""
+    heads = [(1, 3)] if w.d == 256 else [(0, 0), (w.B - 1, w.Hkv - 1)]
+    head_case(w, heads)
+
+
 # ----------------------------------------------------------------------------- pins on the GPU
 def test_bwd_constant_v_and_sums():
     """Constant V: dQ = dK = 0; always: sum_j dV_j = sum_i dO_i per K/V head."""
