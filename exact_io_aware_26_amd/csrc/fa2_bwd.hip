@@ -961,7 +961,6 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
         {
             // Block s - 1 (stages past the last block compute scores nobody reads).
             int kb0;
-            const bool own = true;     // every list entry is needed by the workgroup's rows
             if constexpr (SPARSE) {
                 const int bi = min(max(s - 1, 0), n_kb - 1);
                 const int e = __builtin_amdgcn_readfirstlane((int)tl[bi >> 1]);
@@ -969,12 +968,7 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
             } else {
                 kb0 = 32 * (s - 1);
             }
-            if (!own) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) sc[P_EL][u][i] = -kInf;
-            } else if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
+            if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     // Element i holds key kb0 + 4g + 8 (i / 4) + i % 4: masked when
