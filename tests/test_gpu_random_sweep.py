@@ -6,6 +6,8 @@ either the dense path (forward and backward) or a block mask (random, local
 + global, diagonal, strided, key block 0 only, or all zeros; d <= 128).
 Every draw goes through the same checks as the dedicated GPU tests.  The
 draws come from a fixed seed, so the set of shapes is the same on every run.
+A second set of 100 dense draws (its own fixed seed) runs through the
+binary16 entry points.
 
 The dQ gate can be missed, rarely, on a dense shape (measured: about 1 in
 365 random shapes; none here).  dQ inherits the bf16 rounding of the stored
@@ -21,6 +23,7 @@ import pytest
 
 from tests import test_gpu_backward as tb
 from tests import test_gpu_block_sparse as ts
+from tests import test_gpu_f16 as th
 from tests import test_gpu_forward as tf
 from tests.parity import log
 
@@ -28,14 +31,15 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 SEED, CHUNKS, PER_CHUNK = 11, 20, 20
+SEED_F16, CHUNKS_F16 = 12, 5
 KINDS = ["dense", "dense", "dense", "random", "random", "local_global", "diagonal", "strided", "column0", "zeros"]
 NS = [1, 3, 31, 64, 97, 128, 191, 256, 300, 383, 449, 512, 640, 777]
 
 
-def draws():
-    rng = random.Random(SEED)
+def draws(seed=SEED, count=CHUNKS * PER_CHUNK):
+    rng = random.Random(seed)
     out = []
-    for c in range(CHUNKS * PER_CHUNK):
+    for c in range(count):
         d = rng.choice([64, 128, 256])
         N = rng.choice(NS + [1024 + rng.randrange(64)])
         Hkv = rng.choice([1, 2, 3])
@@ -48,6 +52,8 @@ def draws():
 
 
 DRAWS = draws()
+# Dense shapes for the binary16 entry points (the kind drawn is not used).
+DRAWS_F16 = draws(SEED_F16, CHUNKS_F16 * PER_CHUNK)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -68,3 +74,11 @@ def test_random_sweep(chunk):
             ts.check_case(seed, B, Hq, Hkv, N, d, causal, kind)
         else:
             log(f"[sweep] seed={seed}: block masks are d <= 128 only, skipped")
+
+
+@pytest.mark.parametrize("chunk", range(CHUNKS_F16))
+def test_random_sweep_f16(chunk):
+    """The same kind of draws through fa2_fwd_f16 / fa2_bwd_f16, dense only."""
+    for seed, B, Hq, Hkv, N, d, causal, _ in DRAWS_F16[chunk * PER_CHUNK:(chunk + 1) * PER_CHUNK]:
+        th.fwd_case(seed, B, Hq, Hkv, N, d, causal)
+        th.bwd_case(seed, B, Hq, Hkv, N, d, causal)
