@@ -217,12 +217,84 @@ int oracle_fwd_rows(const double *Q, const double *K, const double *V,
 }
 
 /*
+ * Gradients of one key/value head (b, hk) from the row statistics of its G
+ * query heads: Lst [G*N] the logsumexp L_i and Dst [G*N] the D_i of each
+ * query row.  P_ij = exp(S_ij - L_i), dS_ij = P_ij (dP_ij - D_i).  Two
+ * passes over the plain definitions: dQ by rows, then dK/dV by key columns
+ * (so no two threads write one location).
+ */
+static void grads_from_stats(const double *Q, const double *K, const double *V,
+                             const double *dO, int Hq, int Hkv, int N, int d,
+                             const mask_t *mk, double scale, int b, int hk,
+                             const double *Lst, const double *Dst,
+                             double *dQg, double *dKh, double *dVh)
+{
+    const int G = Hq / Hkv;
+    const double *Kh = head_ptr(K, b, hk, Hkv, N, d);
+    const double *Vh = head_ptr(V, b, hk, Hkv, N, d);
+
+    /* dQ_i = scale * sum_j dS_ij K_j. */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (long r = 0; r < (long)G * N; ++r) {
+            int g = (int)(r / N), i = (int)(r % N);
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *q = Qh + (size_t)i * d;
+            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+            double *dq = dQg + (size_t)r * d;
+            for (int t = 0; t < d; ++t) dq[t] = 0.0;
+            for (int j = 0; j < N; ++j) {
+                double sij = score(q, Kh + (size_t)j * d, d, scale, mk, i, j);
+                double p = prob(sij, Lst[r]);
+                if (p == 0.0) continue;
+                const double *v = Vh + (size_t)j * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                double ds = p * (dp - Dst[r]);
+                const double *k = Kh + (size_t)j * d;
+                for (int t = 0; t < d; ++t) dq[t] += ds * k[t];
+            }
+            for (int t = 0; t < d; ++t) dq[t] *= scale;
+    }
+
+    /* dK_j = scale * sum_g sum_i dS_ij Q_i ;  dV_j = sum_g sum_i P_ij dO_i. */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int j = 0; j < N; ++j) {
+        const double *k = Kh + (size_t)j * d;
+        const double *v = Vh + (size_t)j * d;
+        double *dk = dKh + (size_t)j * d;
+        double *dv = dVh + (size_t)j * d;
+        for (int t = 0; t < d; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
+        for (int g = 0; g < G; ++g) {
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
+            for (int i = 0; i < N; ++i) {
+                const double *q = Qh + (size_t)i * d;
+                double sij = score(q, k, d, scale, mk, i, j);
+                double p = prob(sij, Lst[(long)g * N + i]);
+                if (p == 0.0) continue;
+                const double *dOr = dOh + (size_t)i * d;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
+                double ds = p * (dp - Dst[(long)g * N + i]);
+                for (int t = 0; t < d; ++t) {
+                    dv[t] += p * dOr[t];
+                    dk[t] += ds * q[t];
+                }
+            }
+        }
+        for (int t = 0; t < d; ++t) dk[t] *= scale;
+    }
+}
+
+/*
  * Backward of one key/value head (b, hk) and the G query heads that share it.
  *   dQg [G, N, d]  dQ of query heads hk*G .. hk*G+G-1
  *   dKh, dVh [N, d]
  *   Lg, Dg [G, N]  the statistics L and D of those query heads (may be NULL)
- * Three passes, each over the plain definitions: row statistics, then dQ by
- * rows, then dK/dV by key columns (so no two threads write one location).
+ * The row statistics L_i and D_i = sum_j P_ij dP_ij first, then the
+ * gradients from them (grads_from_stats).
  */
 static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
                             const double *dO, int Hq, int Hkv, int N, int d,
@@ -262,59 +334,7 @@ static void bwd_one_kv_head(const double *Q, const double *K, const double *V,
         free(s);
     }
 
-    /* Pass 2: dQ_i = scale * sum_j dS_ij K_j. */
-    #pragma omp parallel for schedule(dynamic, 8)
-    for (long r = 0; r < (long)G * N; ++r) {
-            int g = (int)(r / N), i = (int)(r % N);
-            int hq = hk * G + g;
-            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
-            const double *q = Qh + (size_t)i * d;
-            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
-            double *dq = dQg + (size_t)r * d;
-            for (int t = 0; t < d; ++t) dq[t] = 0.0;
-            for (int j = 0; j < N; ++j) {
-                double sij = score(q, Kh + (size_t)j * d, d, scale, mk, i, j);
-                double p = prob(sij, Lst[r]);
-                if (p == 0.0) continue;
-                const double *v = Vh + (size_t)j * d;
-                double dp = 0.0;
-                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
-                double ds = p * (dp - Dst[r]);
-                const double *k = Kh + (size_t)j * d;
-                for (int t = 0; t < d; ++t) dq[t] += ds * k[t];
-            }
-            for (int t = 0; t < d; ++t) dq[t] *= scale;
-    }
-
-    /* Pass 3: dK_j = scale * sum_g sum_i dS_ij Q_i ;  dV_j = sum_g sum_i P_ij dO_i. */
-    #pragma omp parallel for schedule(dynamic, 8)
-    for (int j = 0; j < N; ++j) {
-        const double *k = Kh + (size_t)j * d;
-        const double *v = Vh + (size_t)j * d;
-        double *dk = dKh + (size_t)j * d;
-        double *dv = dVh + (size_t)j * d;
-        for (int t = 0; t < d; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
-        for (int g = 0; g < G; ++g) {
-            int hq = hk * G + g;
-            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
-            const double *dOh = head_ptr(dO, b, hq, Hq, N, d);
-            for (int i = 0; i < N; ++i) {
-                const double *q = Qh + (size_t)i * d;
-                double sij = score(q, k, d, scale, mk, i, j);
-                double p = prob(sij, Lst[(long)g * N + i]);
-                if (p == 0.0) continue;
-                const double *dOr = dOh + (size_t)i * d;
-                double dp = 0.0;
-                for (int t = 0; t < d; ++t) dp += dOr[t] * v[t];
-                double ds = p * (dp - Dst[(long)g * N + i]);
-                for (int t = 0; t < d; ++t) {
-                    dv[t] += p * dOr[t];
-                    dk[t] += ds * q[t];
-                }
-            }
-        }
-        for (int t = 0; t < d; ++t) dk[t] *= scale;
-    }
+    grads_from_stats(Q, K, V, dO, Hq, Hkv, N, d, mk, scale, b, hk, Lst, Dst, dQg, dKh, dVh);
 
     if (Lg) memcpy(Lg, Lst, sizeof(double) * (size_t)G * N);
     if (Dg) memcpy(Dg, Dst, sizeof(double) * (size_t)G * N);
@@ -445,37 +465,21 @@ int oracle_fwd_bf16(const double *Q, const double *K, const double *V, double *O
     return 0;
 }
 
-/* Working-precision backward of one key/value head (b, hk): dQg [G,N,d] of
- * query heads hk*G.., dKh and dVh [N,d]. */
-static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double *V,
-                                 const double *dO, int Hq, int Hkv, int N, int d,
-                                 const mask_t *mk, double scale, int b, int hk,
-                                 double *dQg, double *dKh, double *dVh, double *Dg)
+/*
+ * Working-precision gradients of one key/value head (b, hk) from row
+ * statistics Lst (L_i) and Dst (D_i) of its G query heads [G*N]: as
+ * grads_from_stats, with P rounded to bf16 in dV and dS rounded to bf16 in
+ * dQ and dK.
+ */
+static void grads_from_stats_bf16(const double *Q, const double *K, const double *V,
+                                  const double *dO, int Hq, int Hkv, int N, int d,
+                                  const mask_t *mk, double scale, int b, int hk,
+                                  const double *Lst, const double *Dst,
+                                  double *dQg, double *dKh, double *dVh)
 {
     const int G = Hq / Hkv;
     const double *Kh = head_ptr(K, b, hk, Hkv, N, d);
     const double *Vh = head_ptr(V, b, hk, Hkv, N, d);
-    double *Lst = (double *)malloc(sizeof(double) * (size_t)G * N);
-    double *Dst = (double *)malloc(sizeof(double) * (size_t)G * N);
-    /* L_i and D_i = dO_i . bf16(O_i), with O_i from the working-precision forward. */
-    #pragma omp parallel
-    {
-        double *s = (double *)malloc(sizeof(double) * (size_t)N);
-        double *o = (double *)malloc(sizeof(double) * (size_t)d);
-        #pragma omp for schedule(dynamic, 8)
-        for (long r = 0; r < (long)G * N; ++r) {
-            int g = (int)(r / N), i = (int)(r % N);
-            int hq = hk * G + g;
-            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
-            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
-            Lst[r] = row_forward_bf16(Qh, Kh, Vh, N, d, scale, mk, i, s, o);
-            double D = 0.0;
-            for (int t = 0; t < d; ++t) D += dOr[t] * round_bf16(o[t]);
-            Dst[r] = D;
-        }
-        free(s);
-        free(o);
-    }
     /* dQ_i = scale * sum_j bf16(dS_ij) K_j */
     #pragma omp parallel for schedule(dynamic, 8)
     for (long r = 0; r < (long)G * N; ++r) {
@@ -526,6 +530,40 @@ static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double 
         }
         for (int t = 0; t < d; ++t) dk[t] *= scale;
     }
+}
+
+/* Working-precision backward of one key/value head (b, hk): dQg [G,N,d] of
+ * query heads hk*G.., dKh and dVh [N,d]. */
+static void bwd_bf16_one_kv_head(const double *Q, const double *K, const double *V,
+                                 const double *dO, int Hq, int Hkv, int N, int d,
+                                 const mask_t *mk, double scale, int b, int hk,
+                                 double *dQg, double *dKh, double *dVh, double *Dg)
+{
+    const int G = Hq / Hkv;
+    const double *Kh = head_ptr(K, b, hk, Hkv, N, d);
+    const double *Vh = head_ptr(V, b, hk, Hkv, N, d);
+    double *Lst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    double *Dst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    /* L_i and D_i = dO_i . bf16(O_i), with O_i from the working-precision forward. */
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 8)
+        for (long r = 0; r < (long)G * N; ++r) {
+            int g = (int)(r / N), i = (int)(r % N);
+            int hq = hk * G + g;
+            const double *Qh = head_ptr(Q, b, hq, Hq, N, d);
+            const double *dOr = head_ptr(dO, b, hq, Hq, N, d) + (size_t)i * d;
+            Lst[r] = row_forward_bf16(Qh, Kh, Vh, N, d, scale, mk, i, s, o);
+            double D = 0.0;
+            for (int t = 0; t < d; ++t) D += dOr[t] * round_bf16(o[t]);
+            Dst[r] = D;
+        }
+        free(s);
+        free(o);
+    }
+    grads_from_stats_bf16(Q, K, V, dO, Hq, Hkv, N, d, mk, scale, b, hk, Lst, Dst, dQg, dKh, dVh);
     if (Dg) memcpy(Dg, Dst, sizeof(double) * (size_t)G * N);
     free(Lst);
     free(Dst);
@@ -561,6 +599,70 @@ int oracle_bwd_bf16_head(const double *Q, const double *K, const double *V,
     if (N == 0) return 0;
     bwd_bf16_one_kv_head(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk, dQg, dKh, dVh, NULL);
     return 0;
+}
+
+/*
+ * The backward from a forward's saved outputs, the way the method runs it
+ * (summary page, section 4 symbol table: P is rebuilt from the saved
+ * logsumexp L, and D = rowsum(dO o O) is formed from the saved O).  For
+ * given O [B,Hq,N,d] and L [B,Hq,N]:
+ *   P_ij = exp(S_ij - L_i),  D_i = sum_t dO_it O_it,  dS_ij = P_ij (dP_ij - D_i),
+ *   dQ, dK, dV as in the definition above, in fp64.
+ * With the exact forward's O and L this is oracle_bwd.  With a stored
+ * (rounded) O it is the exact gradient the method computes from that O: the
+ * difference from oracle_bwd is then the effect of O's rounding through D.
+ * A row with L_i = -inf (every score masked) has P_i = 0, dQ_i = 0.
+ * oracle_bwd_given_bf16 is the same at the method's working precision: P
+ * rounded to bf16 in dV, dS rounded to bf16 in dQ and dK (results unrounded).
+ */
+static int bwd_given(const double *Q, const double *K, const double *V,
+                     const double *O, const double *L, const double *dO,
+                     double *dQ, double *dK, double *dV, int B, int Hq, int Hkv,
+                     int N, int d, int causal, const unsigned char *bm, double scale,
+                     int working_precision)
+{
+    const mask_t mk = {causal, bm, (N + ORACLE_SPARSE_BLOCK - 1) / ORACLE_SPARSE_BLOCK};
+    if (check_sizes(B, Hq, Hkv, N, d)) return -1;
+    if ((long)B * Hq * N == 0) return 0;
+    const int G = Hq / Hkv;
+    double *Dst = (double *)malloc(sizeof(double) * (size_t)G * N);
+    for (int b = 0; b < B; ++b)
+        for (int hk = 0; hk < Hkv; ++hk) {
+            const size_t row0 = ((size_t)b * Hq + (size_t)hk * G) * (size_t)N;
+            for (long r = 0; r < (long)G * N; ++r) {
+                const double *o = O + (row0 + (size_t)r) * d;
+                const double *g = dO + (row0 + (size_t)r) * d;
+                double D = 0.0;
+                for (int t = 0; t < d; ++t) D += g[t] * o[t];
+                Dst[r] = D;
+            }
+            const double *Lg = L + row0;
+            const size_t koff = (((size_t)b * Hkv + hk) * (size_t)N) * d;
+            if (working_precision)
+                grads_from_stats_bf16(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk, Lg, Dst,
+                                      dQ + row0 * d, dK + koff, dV + koff);
+            else
+                grads_from_stats(Q, K, V, dO, Hq, Hkv, N, d, &mk, scale, b, hk, Lg, Dst,
+                                 dQ + row0 * d, dK + koff, dV + koff);
+        }
+    free(Dst);
+    return 0;
+}
+
+int oracle_bwd_given(const double *Q, const double *K, const double *V,
+                     const double *O, const double *L, const double *dO,
+                     double *dQ, double *dK, double *dV, int B, int Hq, int Hkv,
+                     int N, int d, int causal, const unsigned char *bm, double scale)
+{
+    return bwd_given(Q, K, V, O, L, dO, dQ, dK, dV, B, Hq, Hkv, N, d, causal, bm, scale, 0);
+}
+
+int oracle_bwd_given_bf16(const double *Q, const double *K, const double *V,
+                          const double *O, const double *L, const double *dO,
+                          double *dQ, double *dK, double *dV, int B, int Hq, int Hkv,
+                          int N, int d, int causal, const unsigned char *bm, double scale)
+{
+    return bwd_given(Q, K, V, O, L, dO, dQ, dK, dV, B, Hq, Hkv, N, d, causal, bm, scale, 1);
 }
 
 int oracle_num_threads(void)

@@ -52,12 +52,16 @@ def _open(path: str):
                                ctypes.c_double]
     lib.oracle_bwd_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double,
                                     i, i, dp, dp, dp, dp, dp]
+    lib.oracle_bwd_given.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, bm,
+                                     ctypes.c_double]
+    lib.oracle_bwd_given_bf16.argtypes = lib.oracle_bwd_given.argtypes
     lib.oracle_fwd_bf16.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double]
     lib.oracle_bwd_bf16.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, bm,
                                     ctypes.c_double]
     lib.oracle_bwd_bf16_head.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, bm, ctypes.c_double,
                                          i, i, dp, dp, dp]
-    for f in (lib.oracle_fwd, lib.oracle_fwd_rows, lib.oracle_bwd, lib.oracle_bwd_head,
+    for f in (lib.oracle_fwd, lib.oracle_fwd_rows, lib.oracle_bwd, lib.oracle_bwd_head, lib.oracle_bwd_given,
+              lib.oracle_bwd_given_bf16,
               lib.oracle_fwd_bf16, lib.oracle_bwd_bf16, lib.oracle_bwd_bf16_head):
         f.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -212,6 +216,31 @@ def backward_head(q, k, v, do, b: int, hk: int, causal: bool = False,
     if rc != 0:
         raise ValueError("oracle_bwd_head: bad sizes or head index")
     return dq, dk, dv, L, D
+
+
+def backward_given(q, k, v, o, L, do, causal: bool = False, scale: float | None = None, lib=None,
+                   block_mask=None, working_precision: bool = False):
+    """The backward from given forward outputs o [B,Hq,N,d] and L [B,Hq,N]:
+    P = exp(S - L), D = rowsum(do * o) from the given o.  Returns (dQ, dK, dV).
+    ``working_precision``: P and dS rounded to bf16 before their products (the
+    method's operand precision), results unrounded."""
+    lib = lib or load()
+    q, k, v, o, L, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(L), _f64(do)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    if o.shape != q.shape or do.shape != q.shape or L.shape != (B, Hq, N):
+        raise ValueError("o and do must be shaped like q, L like [B, Hq, N]")
+    bm = _mask(block_mask, N)
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    fn = lib.oracle_bwd_given_bf16 if working_precision else lib.oracle_bwd_given
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, Hq, Hkv, N, d, int(causal), _mptr(bm), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_bwd_given: bad sizes")
+    return dq, dk, dv
 
 
 def forward_bf16(q, k, v, causal: bool = False, scale: float | None = None, lib=None, block_mask=None):

@@ -3,7 +3,9 @@
 Each ``pin_*`` function takes a loaded oracle library and raises
 AssertionError when the oracle disagrees with:
 
-- a hand-derived worked example (``tests/golden/two_key_example.json``),
+- hand-derived worked examples (``tests/golden/two_key_example.json``, and
+  ``two_key_ds_example.json``, whose P and dS are not bf16-exact, for the
+  working-precision roundings),
 - an independent library implementation (PyTorch's CPU scaled-dot-product
   attention and autograd, float64),
 - central finite differences of its own forward (for the gradients),
@@ -12,6 +14,11 @@ AssertionError when the oracle disagrees with:
 - invariants of the definition (rows of P sum to one, constant V, shifting
   keys, permuting keys, GQA equals repeated K/V heads, column sums of dV,
   causal row 0, D = rowsum(dO * O)),
+- rigorous round-to-nearest-even error bounds of the working-precision
+  variant (P in the forward and in dV, dS in dQ and dK), which must also be
+  approached,
+- for the backward from given forward outputs: PyTorch autograd (exact O, L),
+  a shift of D through O, a shift of L, and the same rounding bounds,
 - for block-sparse attention, PyTorch with the equivalent element mask,
   dense attention (all-ones mask) and attention over a subset of the rows
   (rows the mask empties).
@@ -78,6 +85,44 @@ def pin_golden_two_key(lib):
         _close(dq.reshape(2, 1), exp["dQ"], 1e-14, f"golden {key} dQ")
         _close(dk.reshape(2, 1), exp["dK"], 1e-14, f"golden {key} dK")
         _close(dv.reshape(2, 1), exp["dV"], 1e-14, f"golden {key} dV")
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    arrays = [np.array(_golden_value(g[n])).reshape(1, 1, 2, 1) for n in ("Q", "K", "V", "dO")]
+    return g, arrays
+
+
+def pin_golden_ds_example(lib):
+    """Second hand-derived example: row 1 has P = (1/3, 2/3), so P and dS are not
+    bf16-exact and the working-precision backward must round them (dV from
+    bf16(P), dQ and dK from bf16(dS)).  Also pins the backward from given O and L."""
+    g, (q, k, v, do) = _load_golden("two_key_ds_example.json")
+    for causal, key in ((False, "noncausal"), (True, "causal")):
+        exp = {n: np.array(_golden_value(val)) for n, val in g[key].items()}
+        wp = {n: np.array(_golden_value(val)) for n, val in g["working_precision"][key].items()}
+        o, L = orc.forward(q, k, v, causal, g["scale"], lib=lib)
+        _close(o.reshape(2, 1), exp["O"], 1e-14, f"ds golden {key} O")
+        _close(L.reshape(2), exp["L"], 1e-14, f"ds golden {key} L")
+        dq, dk, dv, D = orc.backward(q, k, v, do, causal, g["scale"], lib=lib)
+        _close(D.reshape(2), exp["D"], 1e-14, f"ds golden {key} D")
+        for n, a in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            _close(a.reshape(2, 1), exp[n], 1e-14, f"ds golden {key} {n}")
+        ob, _ = orc.forward_bf16(q, k, v, causal, g["scale"], lib=lib)
+        _close(ob.reshape(2, 1), wp["O"], 1e-14, f"ds golden working-precision {key} O")
+        for n, a in zip(("dQ", "dK", "dV"), orc.backward_bf16(q, k, v, do, causal, g["scale"], lib=lib)):
+            _close(a.reshape(2, 1), wp[n], 1e-14, f"ds golden working-precision {key} {n}")
+        # The backward from given O and L: the exact forward's outputs give the exact
+        # gradients, and at working precision the rounded ones.
+        o_given, L_given = exp["O"].reshape(1, 1, 2, 1), exp["L"].reshape(1, 1, 2)
+        for n, a in zip(("dQ", "dK", "dV"),
+                        orc.backward_given(q, k, v, o_given, L_given, do, causal, g["scale"], lib=lib)):
+            _close(a.reshape(2, 1), exp[n], 1e-14, f"ds golden given {key} {n}")
+        for n, a in zip(("dQ", "dK", "dV"),
+                        orc.backward_given(q, k, v, o_given, L_given, do, causal, g["scale"], lib=lib,
+                                           working_precision=True)):
+            _close(a.reshape(2, 1), wp[n], 1e-14, f"ds golden given working-precision {key} {n}")
 
 
 # ----------------------------------------------------------------------------
@@ -374,7 +419,21 @@ def pin_working_precision(lib):
         assert ratio.max() <= 1.0 + 1e-9, f"dV rounding above its bound: {ratio.max()}"
         assert ratio.max() >= 0.25, f"dV rounding far below its bound: {ratio.max()}"
         # D is formed from the stored (bf16) O of the working-precision forward.
-        _, _, _, D_b = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib, return_d=True)
+        dq_b, dk_b, _, D_b = orc.backward_bf16(q, k, v, do, causal, scale, lib=lib, return_d=True)
+        # dQ and dK: the products take bf16(dS) with dS = P o (dP - D) at that D; each
+        # element is off by at most U * scale * sum |dS| |K| (|Q|) from the unrounded
+        # products, and must come close to that bound.
+        dP = np.einsum("bhid,bhjd->bhij", do, vr)
+        dS = P * (dP - D_b[..., None])
+        dq_u = scale * np.einsum("bhij,bhjd->bhid", dS, kr)
+        dk_u = scale * np.einsum("bhij,bhid->bhjd", dS, q).reshape(B, Hkv, 2, N, d).sum(2)
+        for name, got, unr, bound in (
+                ("dQ", dq_b, dq_u, U_BF16 * scale * np.einsum("bhij,bhjd->bhid", np.abs(dS), np.abs(kr))),
+                ("dK", dk_b, dk_u, U_BF16 * scale * np.einsum("bhij,bhid->bhjd", np.abs(dS), np.abs(q))
+                 .reshape(B, Hkv, 2, N, d).sum(2))):
+            ratio = np.abs(got - unr) / np.maximum(bound, 1e-300)
+            assert ratio.max() <= 1.0 + 1e-9, f"{name} dS rounding above its bound: {ratio.max()}"
+            assert ratio.max() >= 0.25, f"{name} dS rounding far below its bound: {ratio.max()}"
         o_stored = o_b.astype(np.float32).view(np.uint32).astype(np.uint64)
         o_stored = (((o_stored + 0x7FFF + ((o_stored >> 16) & 1)) >> 16) << 16).astype(np.uint32)
         o_stored = o_stored.view(np.float32).astype(np.float64)
@@ -386,6 +445,62 @@ def pin_working_precision(lib):
         _close(hq_, dq_b[0], 0, "bf16 head dQ")
         _close(hk_, dk_b[0, 0], 0, "bf16 head dK")
         _close(hv_, dv_b2[0, 0], 0, "bf16 head dV")
+
+
+# ----------------------------------------------------------------------------
+# 6b. the backward from given forward outputs (O, L)
+# ----------------------------------------------------------------------------
+def pin_backward_given(lib):
+    """P is rebuilt from the given L and D is formed from the given O:
+    - with the exact forward's O and L it equals PyTorch's fp64 autograd;
+    - moving O_i along dO_i so that D_i shifts by c_i leaves dV unchanged, leaves dQ_i
+      unchanged where c_i = 0, and (rows of P summing to one) gives
+      sum_j dS_ij = -c_i, so sum_j dK_j = -scale * sum_i c_i Q_i per K/V head;
+    - raising every L_i by c scales P, hence dV, by exp(-c);
+    - at working precision, each gradient is within the RNE bound of its rounded
+      operand (P for dV, dS for dQ and dK) of the exact one and comes close to it."""
+    rng = np.random.default_rng(18)
+    B, Hq, Hkv, N, d = 2, 4, 2, 29, 6
+    G = Hq // Hkv
+    q, k, v = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    do = _rand(rng, B, Hq, N, d)
+    scale = 0.85
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal in (False, True):
+        tag = f"causal{int(causal)}"
+        o, L = orc.forward(q, k, v, causal, scale, lib=lib)
+        dq, dk, dv = orc.backward_given(q, k, v, o, L, do, causal, scale, lib=lib)
+        to, _, tdq, tdk, tdv = _torch_reference(q, k, v, causal, scale, do)
+        _close(dq, tdq, 1e-11, f"given dQ vs torch {tag}")
+        _close(dk, tdk, 1e-11, f"given dK vs torch {tag}")
+        _close(dv, tdv, 1e-11, f"given dV vs torch {tag}")
+        c = rng.standard_normal((B, Hq, N))
+        c[:, :, ::3] = 0.0
+        o2 = o + c[..., None] * do / np.sum(do * do, axis=-1, keepdims=True)
+        dq2, dk2, dv2 = orc.backward_given(q, k, v, o2, L, do, causal, scale, lib=lib)
+        _close(dv2, dv, 1e-13, f"given D shift leaves dV {tag}")
+        _close(dq2[:, :, ::3], dq[:, :, ::3], 1e-12, f"given D shift leaves dQ of unshifted rows {tag}")
+        assert np.max(np.abs(dq2 - dq)) > 1e-3, f"given O ignored in dQ {tag}"
+        want = -scale * np.einsum("bhi,bhid->bhd", c, q).reshape(B, Hkv, G, d).sum(2)
+        _close(dk2.sum(axis=2), want, 1e-12, f"given D shift: column sum of dK {tag}")
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, d)), 1e-12, f"given exact: column sum of dK {tag}")
+        _, _, dv3 = orc.backward_given(q, k, v, o, L + 0.4, do, causal, scale, lib=lib)
+        _close(dv3, math.exp(-0.4) * dv, 1e-13, f"given L shift scales dV {tag}")
+        # Working precision from the same given O and L.
+        s = scale * np.einsum("bhid,bhjd->bhij", q, kr)
+        if causal:
+            s = np.where(np.triu(np.ones((N, N), bool), 1), -np.inf, s)
+        P = np.exp(s - L[..., None])
+        dS = P * (np.einsum("bhid,bhjd->bhij", do, vr) - np.sum(do * o, axis=-1)[..., None])
+        wq, wk, wv = orc.backward_given(q, k, v, o, L, do, causal, scale, lib=lib, working_precision=True)
+        sum_g = lambda x: x.reshape(B, Hkv, G, N, d).sum(2)
+        for name, got, ex, bound in (
+                ("dV", wv, dv, U_BF16 * sum_g(np.einsum("bhij,bhid->bhjd", P, np.abs(do)))),
+                ("dQ", wq, dq, U_BF16 * scale * np.einsum("bhij,bhjd->bhid", np.abs(dS), np.abs(kr))),
+                ("dK", wk, dk, U_BF16 * scale * sum_g(np.einsum("bhij,bhid->bhjd", np.abs(dS), np.abs(q))))):
+            ratio = np.abs(got - ex) / np.maximum(bound, 1e-300)
+            assert ratio.max() <= 1.0 + 1e-9, f"given working-precision {name} above its bound {tag}: {ratio.max()}"
+            assert ratio.max() >= 0.25, f"given working-precision {name} far below its bound {tag}: {ratio.max()}"
 
 
 # ----------------------------------------------------------------------------
@@ -504,6 +619,6 @@ def pin_block_sparse(lib):
         _close(bv_, wv[0, 0], 0, f"{case}: backward_bf16_head dV")
 
 
-ALL_PINS = [pin_golden_two_key, pin_torch_forward, pin_torch_backward,
+ALL_PINS = [pin_golden_two_key, pin_golden_ds_example, pin_torch_forward, pin_torch_backward,
             pin_finite_differences, pin_closed_forms, pin_invariants,
-            pin_sampled_entry_points, pin_working_precision, pin_block_sparse]
+            pin_sampled_entry_points, pin_working_precision, pin_backward_given, pin_block_sparse]

@@ -43,8 +43,8 @@ MUTATIONS = [
     ("dQ built from Q instead of K",
      "double ds = p * (dp - Dst[r]);\n                const double *k = Kh + (size_t)j * d;\n                for (int t = 0; t < d; ++t) dq[t] += ds * k[t];",
      "double ds = p * (dp - Dst[r]);\n                const double *k = Kh + (size_t)j * d;\n                for (int t = 0; t < d; ++t) dq[t] += ds * q[t];"),
-    ("scale missing from dK", "for (int t = 0; t < d; ++t) dk[t] *= scale;\n    }\n\n    if (Lg)",
-     "\n    }\n\n    if (Lg)"),
+    ("scale missing from dK", "for (int t = 0; t < d; ++t) dk[t] *= scale;\n    }\n}\n\n/*\n * Backward of one",
+     "\n    }\n}\n\n/*\n * Backward of one"),
     ("dV uses the key-side row of dO (transposed operand)", "dv[t] += p * dOr[t];",
      "dv[t] += p * dOh[(size_t)j * d + t];"),
     ("dK sums over one query head of the group only",
@@ -57,6 +57,16 @@ MUTATIONS = [
     ("bf16 rounding dropped from P of the working-precision dV", "double pb = round_bf16(p);\n                double ds",
      "double pb = p;\n                double ds"),
     ("working-precision D from the unrounded O", "D += dOr[t] * round_bf16(o[t]);", "D += dOr[t] * o[t];"),
+    ("working-precision dS rounding dropped before dQ", "double ds = round_bf16(p * (dp - Dst[r]));",
+     "double ds = p * (dp - Dst[r]);"),
+    ("working-precision dS rounding dropped before dK",
+     "double ds = round_bf16(p * (dp - Dst[(long)g * N + i]));", "double ds = p * (dp - Dst[(long)g * N + i]);"),
+    ("backward from given outputs: the given O ignored in D", "for (int t = 0; t < d; ++t) D += g[t] * o[t];",
+     "for (int t = 0; t < d; ++t) D += 0.0 * o[t];"),
+    ("backward from given outputs: L of the wrong head group", "const double *Lg = L + row0;",
+     "const double *Lg = L + (size_t)b * Hq * N;"),
+    ("backward from given outputs: working precision ignored", "if (working_precision)\n",
+     "if (0)\n"),
 ]
 
 
