@@ -115,21 +115,21 @@ struct WorkspaceLayout {
     size_t d_off, l2_off, dq_off, total;
 };
 
-// D [B*Hq*Npad] fp32, then L * log2(e) [B*Hq*Npad] fp32, then the dQ
-// accumulator [B*Hq*N*d] fp32, each on a 256-byte boundary.
-WorkspaceLayout workspace_layout(uint64_t rows_pad, uint64_t q_elems) {
+// D [B*Hq*Npad] fp32, then L * log2(e) [B*Hq*Npad] fp32, each on a 256-byte
+// boundary; in the atomic-dQ mode also the dQ accumulator [B*Hq*N*d] fp32.
+WorkspaceLayout workspace_layout(uint64_t rows_pad, uint64_t q_elems, bool atomic) {
     WorkspaceLayout w;
     w.d_off = 0;
     w.l2_off = align_up(rows_pad * 4, kWorkspaceAlign);
     w.dq_off = w.l2_off + align_up(rows_pad * 4, kWorkspaceAlign);
-    w.total = w.dq_off + align_up(q_elems * 4, kWorkspaceAlign);
+    w.total = w.dq_off + (atomic ? align_up(q_elems * 4, kWorkspaceAlign) : 0);
     return w;
 }
 
 fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                         const void* dO, const void* dQ, const void* dK, const void* dV,
                         const void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
-                        float scale, bool* empty, Sizes* sz) {
+                        float scale, bool atomic, bool* empty, Sizes* sz) {
     fa2_status s = check_problem(B, Hq, Hkv, N, d, scale, empty, sz);
     if (s != FA2_OK || *empty) return s;
     const void* ptrs[9] = {Q, K, V, O, L, dO, dQ, dK, dV};
@@ -141,7 +141,7 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
     if (!ws) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) != 0)
         return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    const WorkspaceLayout wl = workspace_layout(sz->rows_pad, sz->q_elems);
+    const WorkspaceLayout wl = workspace_layout(sz->rows_pad, sz->q_elems, atomic);
     if (ws_bytes < wl.total) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace too small");
     const uint64_t qb = sz->q_elems * 2, kb = sz->kv_elems * 2, lb = sz->rows * 4;
     const void* ins[6] = {Q, K, V, O, L, dO};
@@ -212,10 +212,11 @@ fa2_status fa2_validate_bwd(const void* Q, const void* K, const void* V, const v
     bool empty;
     Sizes sz;
     return validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq, Hkv, N,
-                        d, scale, &empty, &sz);
+                        d, scale, false, &empty, &sz);
 }
 
-size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+size_t fa2_bwd_stages_workspace_bytes(unsigned stages, int B, int Hq, int Hkv, int N, int d) {
+    if ((stages & FA2_BWD_ALL) == 0 || (stages & ~(FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC)) != 0) return 0;
     if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return 0;
     if (B == 0 || Hq == 0 || N == 0) return 0;
     if (Hkv < 1 || Hq % Hkv != 0) return 0;
@@ -223,7 +224,11 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
     if (N > kMaxN || !count4(B, Hq, N, d, &q_elems) || !count4(B, Hq, padded_rows(N), 1, &rows_pad) ||
         q_elems > (UINT64_MAX >> 3) || rows_pad > (UINT64_MAX >> 4))
         return 0;
-    return workspace_layout(rows_pad, q_elems).total;
+    return workspace_layout(rows_pad, q_elems, (stages & FA2_BWD_DQ_ATOMIC) != 0).total;
+}
+
+size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+    return fa2_bwd_stages_workspace_bytes(FA2_BWD_ALL, B, Hq, Hkv, N, d);
 }
 
 }  // extern "C"
@@ -280,10 +285,11 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
                     "stage mask must hold at least one stage of FA2_BWD_ALL and no unknown bits");
     bool empty;
     Sizes sz;
+    const bool atomic = (stages & FA2_BWD_DQ_ATOMIC) != 0;
     fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
-                                Hkv, N, d, scale, &empty, &sz);
+                                Hkv, N, d, scale, atomic, &empty, &sz);
     if (s != FA2_OK || empty) return s;
-    const WorkspaceLayout wl = workspace_layout(sz.rows_pad, sz.q_elems);
+    const WorkspaceLayout wl = workspace_layout(sz.rows_pad, sz.q_elems, atomic);
     if (sparse) {
         const void* outs[4] = {dQ, dK, dV, workspace};
         const uint64_t ob[4] = {sz.q_elems * 2, sz.kv_elems * 2, sz.kv_elems * 2, wl.total};
@@ -302,7 +308,7 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
     p.dV = static_cast<uint16_t*>(dV);
     p.Dneg = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.d_off);
     p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.l2_off);
-    p.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off);
+    p.dQacc = atomic ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off) : nullptr;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;

@@ -23,7 +23,8 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
-           "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
+           "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes",
+           "fa2_bwd_stages_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
            "fa2_last_error")
 DTYPES = (torch.bfloat16, torch.float16)
 
@@ -69,6 +70,8 @@ def load(path: str | None = None):
     lib.fa2_bwd_block_sparse.restype = i
     lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_bwd_workspace_bytes.restype = sz
+    lib.fa2_bwd_stages_workspace_bytes.argtypes = [ctypes.c_uint, i, i, i, i, i]
+    lib.fa2_bwd_stages_workspace_bytes.restype = sz
     lib.fa2_validate_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
     lib.fa2_validate_fwd.restype = i
     lib.fa2_validate_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f]
@@ -99,9 +102,15 @@ def _stream_handle(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, require_gpu: bool = True):
+    """Check q, k, v and return (B, Hq, Hkv, N, d)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
     if q.dtype not in DTYPES:
         raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+    if require_gpu and not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
@@ -109,12 +118,57 @@ def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
             raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device {q.device}, got {t.device}")
     B, Hq, N, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     return B, Hq, k.shape[1], N, d
+
+
+def _check_tensor(name: str, t, dtype, shape, device) -> None:
+    """A caller-supplied tensor: its dtype, shape, contiguity and device, checked before
+    its pointer reaches the library (which can only check alignment and overlap)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on q's device {device}, got {t.device}")
+
+
+def check_forward_args(q, k, v, out=None, lse=None, require_gpu: bool = True):
+    """The metadata checks of ``forward``: returns (B, Hq, Hkv, N, d).  Raises TypeError
+    or ValueError before anything is allocated or launched."""
+    B, Hq, Hkv, N, d = _dims(q, k, v, require_gpu)
+    if out is not None:
+        _check_tensor("out", out, q.dtype, q.shape, q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, Hq, N), q.device)
+    return B, Hq, Hkv, N, d
+
+
+def check_backward_args(q, k, v, o, lse, do, workspace=None, grads=None, nbytes: int = 0,
+                        require_gpu: bool = True):
+    """The metadata checks of ``backward``: returns (B, Hq, Hkv, N, d)."""
+    B, Hq, Hkv, N, d = _dims(q, k, v, require_gpu)
+    _check_tensor("o", o, q.dtype, q.shape, q.device)
+    _check_tensor("do", do, q.dtype, q.shape, q.device)
+    _check_tensor("lse", lse, torch.float32, (B, Hq, N), q.device)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, torch.uint8, None, q.device)
+        if workspace.dim() != 1 or workspace.numel() < nbytes:
+            raise ValueError(f"workspace must be a 1-D uint8 tensor of at least {nbytes} bytes")
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        for name, t, like in zip(("dq", "dk", "dv"), grads, (q, k, v)):
+            _check_tensor(name, t, q.dtype, like.shape, q.device)
+    return B, Hq, Hkv, N, d
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
@@ -127,15 +181,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     1/sqrt(d).
     """
     lib = load()
-    B, Hq, Hkv, N, d = _dims(q, k, v)
+    B, Hq, Hkv, N, d = check_forward_args(q, k, v, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype")
     fwd = lib.fa2_fwd_f16 if q.dtype == torch.float16 else lib.fa2_fwd
     st = fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
              int(bool(causal)), float(scale), _stream_handle(q))
@@ -143,8 +195,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     return out, lse
 
 
-def workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
-    return load().fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+def workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, stages: int = BWD_ALL) -> int:
+    """Workspace bytes of a backward with these stage bits (the atomic-dQ mode needs more)."""
+    return load().fa2_bwd_stages_workspace_bytes(int(stages), B, Hq, Hkv, N, d)
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -161,25 +214,14 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
-    for name, t in (("o", o), ("do", do)):
-        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped like q, in q's dtype")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+    nbytes = lib.fa2_bwd_stages_workspace_bytes(int(stages), B, Hq, Hkv, N, d)
+    check_backward_args(q, k, v, o, lse, do, workspace, grads, nbytes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    else:
-        dq, dk, dv = grads
-        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-            if t.dtype != q.dtype or t.shape != like.shape or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous tensor shaped like its input, in q's dtype")
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 tensor")
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
+                                                  torch.empty_like(v))
     bwd = lib.fa2_bwd_stages_f16 if q.dtype == torch.float16 else lib.fa2_bwd_stages
     st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
@@ -211,7 +253,7 @@ def forward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
     batch and head.  Rows with no unmasked key get o = 0 and lse = -inf.
     """
     lib = load()
-    B, Hq, Hkv, N, d = _dims(q, k, v)
+    B, Hq, Hkv, N, d = check_forward_args(q, k, v, out, lse)
     if q.dtype != torch.bfloat16:
         raise TypeError("block-sparse attention takes bfloat16 tensors")
     bm = _block_mask(block_mask, N, q.device)
@@ -221,8 +263,6 @@ def forward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype")
     st = lib.fa2_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(bm),
                                   B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
@@ -239,25 +279,14 @@ def backward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
     if q.dtype != torch.bfloat16:
         raise TypeError("block-sparse attention takes bfloat16 tensors")
     bm = _block_mask(block_mask, N, q.device)
-    for name, t in (("o", o), ("do", do)):
-        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped like q, in q's dtype")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+    nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    check_backward_args(q, k, v, o, lse, do, workspace, grads, nbytes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 tensor")
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    else:
-        dq, dk, dv = grads
-        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-            if t.dtype != q.dtype or t.shape != like.shape or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous tensor shaped like its input, in q's dtype")
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
+                                                  torch.empty_like(v))
     st = lib.fa2_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(bm), _ptr(workspace),
                                   workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)),

@@ -86,12 +86,19 @@ fa2_status fa2_fwd(const void *Q, const void *K, const void *V, void *O, float *
 /*
  * Bytes of device workspace fa2_bwd needs: two fp32 [B,Hq,Npad] arrays
  * (Npad = N rounded up to a multiple of 64) holding -D = -rowsum(dO o O) and
- * L * log2(e) per query row, and an fp32 [B,Hq,N,d] array accumulating dQ in
- * the atomic mode, each starting on a 256-byte boundary.  Returns 0 for an
- * empty problem and for sizes fa2_bwd rejects (negative, Hq % Hkv != 0,
+ * L * log2(e) per query row, each starting on a 256-byte boundary.  Returns 0
+ * for an empty problem and for sizes fa2_bwd rejects (negative, Hq % Hkv != 0,
  * N above 2^30, byte counts that overflow).
  */
 size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Bytes of device workspace fa2_bwd_stages / fa2_bwd_stages_f16 need for a
+ * given stage mask (the bits below): those of fa2_bwd_workspace_bytes, plus,
+ * when FA2_BWD_DQ_ATOMIC is set, an fp32 [B,Hq,N,d] dQ accumulator on a
+ * 256-byte boundary after them.  0 for an invalid mask or as above.
+ */
+size_t fa2_bwd_stages_workspace_bytes(unsigned stages, int B, int Hq, int Hkv, int N, int d);
 
 /*
  * Backward pass: dQ, dK, dV of sum(dO o O) for the forward defined above.
@@ -101,8 +108,6 @@ size_t fa2_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *   summed over the Hq/Hkv query heads sharing each key/value head).
  *   workspace: caller-allocated device memory, 256-byte aligned, of at least
  *   fa2_bwd_workspace_bytes(...) bytes; contents undefined on entry and exit.
- *   (The default path uses only its two per-row arrays; the atomic mode of
- *   fa2_bwd_stages also uses the dQ accumulator.)
  * Errors: as fa2_fwd, plus FA2_ERR_INVALID_ARGUMENT when the workspace is
  * NULL, misaligned or too small, or when an output aliases an input or
  * another output.
@@ -130,8 +135,9 @@ fa2_status fa2_bwd(const void *Q, const void *K, const void *V, const void *O,
  * 7) -- the K/V loop adds every tile's dQ contribution into an fp32
  * accumulator in the workspace with atomic adds (PREPROCESS zeroes it,
  * FINALIZE converts it to bf16); dQ is then reproducible only up to the
- * order of those additions.  The mode bit must be the same in every call
- * of one backward pass.
+ * order of those additions, and the workspace must hold
+ * fa2_bwd_stages_workspace_bytes(mask, ...) bytes.  The mode bit must be the
+ * same in every call of one backward pass.
  * Running the three stages in order on one stream, with the same workspace
  * untouched in between, is exactly fa2_bwd (mask FA2_BWD_ALL) or its atomic
  * variant (FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC).  Stages may be issued by

@@ -8,13 +8,18 @@ bf16 value can be within 1e-2 of every exact value there.  The raw max-abs
 error is reported alongside and gated as well wherever every reference
 value is below 2 in magnitude (half an ulp there is at most 0.0039).
 
-For the backward pass the gates may be raised to 1.5x the error of the
-method executed exactly at its working precision (``working=``): the
-method's bf16 operands alone put small causal problems slightly above
-1e-2 beyond rounding.
+Widened gates.  The benchmark configurations are always held to the stated
+gates.  A test of another shape may pass ``working=``, the oracle's result at
+the method's working precision (bf16 P, stored bf16 O and bf16 dS): its gates
+then become 1.5 times the error of that exact bf16 execution where this is
+larger than the stated gate, but never more than a fixed ceiling (``CAP_ATOL``
+for the max-abs gates, ``CAP_RL2`` for relative L2, unless the test states its
+own).  Every widened gate is printed as ``[gate] ...`` with the stated and the
+applied value, and appended to the file named by ``FA2_GATE_LOG`` if set.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -24,6 +29,12 @@ from exact_io_aware_26_amd import inputs
 ATOL_BF16 = 1e-2
 RL2_BF16 = 5e-3
 ATOL_L = 1e-3
+# Ceilings on a widened gate.  The max-abs ceiling covers the method's own
+# error at the default scale (up to about 0.015 beyond rounding on small causal
+# problems, through D formed from the stored bf16 O); the relative-L2 ceiling
+# covers tensors of one or two rows, whose norm is tiny.
+CAP_ATOL = 2e-2
+CAP_RL2 = 4e-2
 
 
 def log(msg: str) -> None:
@@ -56,24 +67,42 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return inputs.bf16_bits_to_f64(inputs.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
 
 
+def _log_gate(name: str, m: dict, stated: tuple, applied: tuple) -> None:
+    w = m["working_precision"]
+    line = (f"[gate] {name}: beyond-rounding stated {stated[0]:.1e} applied {applied[0]:.2e} "
+            f"(working precision {w['max_abs_beyond_rounding']:.2e}, measured {m['max_abs_beyond_rounding']:.2e}); "
+            f"raw stated {stated[1]:.1e} applied {applied[1]:.2e}; "
+            f"rel-L2 stated {stated[2]:.1e} applied {applied[2]:.2e} (measured {m['rel_l2']:.2e})")
+    log(line)
+    path = os.environ.get("FA2_GATE_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
 def check_bf16(name: str, got: np.ndarray, ref: np.ndarray, atol=ATOL_BF16, rl2=RL2_BF16,
-               working: np.ndarray | None = None) -> dict:
+               working: np.ndarray | None = None, cap_atol: float = CAP_ATOL,
+               cap_rl2: float = CAP_RL2) -> dict:
     """Gate a bf16 result against the exact fp64 reference.
 
     ``working`` is the oracle's result at the method's working precision
-    (bf16 P, O and dS at the method's rounding points, see oracle_bwd_bf16).
-    When given, each gate is the stated tolerance or 1.5x the error that an
-    exact execution at that precision makes, whichever is larger: no kernel
-    that uses bf16 operands where the method does can beat that floor.
+    (bf16 P, O and dS at the method's rounding points).  When given, each gate
+    is the stated tolerance or 1.5x the error that an exact execution at that
+    precision makes, whichever is larger, capped at ``cap_atol`` (max-abs) and
+    ``cap_rl2`` (relative L2); a widened gate is logged.
     """
     m = metrics(got, ref)
+    stated = (atol, atol, rl2)
     raw_atol = atol
     if working is not None:
         w = metrics(round_bf16(working), ref)
-        atol = max(atol, 1.5 * w["max_abs_beyond_rounding"])
-        rl2 = max(rl2, 1.5 * w["rel_l2"])
-        raw_atol = max(raw_atol, 1.5 * w["max_abs"])
         m["working_precision"] = w
+        atol = min(cap_atol, max(atol, 1.5 * w["max_abs_beyond_rounding"]))
+        raw_atol = min(cap_atol, max(raw_atol, 1.5 * w["max_abs"]))
+        rl2 = min(cap_rl2, max(rl2, 1.5 * w["rel_l2"]))
+        if (atol, raw_atol, rl2) != stated:
+            _log_gate(name, m, stated, (atol, raw_atol, rl2))
+    m["gate"] = {"beyond_rounding": atol, "raw": raw_atol, "rel_l2": rl2}
     assert m["finite"], f"{name}: non-finite output (unwritten or overflow)"
     assert m["max_abs_beyond_rounding"] <= atol, f"{name}: {m}"
     assert m["rel_l2"] <= rl2, f"{name}: {m}"

@@ -145,10 +145,25 @@ def test_workspace_size(lib):
     rows_pad = B * Hq * ((N + 63) // 64 * 64)   # per-row arrays padded to 64 rows per head
     def up(x):
         return (x + 255) // 256 * 256
-    assert need == 2 * up(rows_pad * 4) + up(rows * d * 4)
+    # The default backward needs the two per-row arrays only.
+    assert need == 2 * up(rows_pad * 4)
     assert vbwd(lib, ws=need - 1) == INVALID
     assert b"workspace" in lib.fa2_last_error()
     assert vbwd(lib, ws=need + 12345) == OK
+    # The atomic-dQ mode also needs the fp32 dQ accumulator, and is checked against it.
+    stages_ws = lib.fa2_bwd_stages_workspace_bytes
+    for mask in (1, 2, 4, 7):
+        assert stages_ws(mask, B, Hq, Hkv, N, d) == need
+    atomic = stages_ws(7 | 8, B, Hq, Hkv, N, d)
+    assert atomic == need + up(rows * d * 4)
+    assert stages_ws(2 | 8, B, Hq, Hkv, N, d) == atomic
+    for bad in (0, 8, 16):
+        assert stages_ws(bad, B, Hq, Hkv, N, d) == 0
+    p = [addr(i) for i in range(10)]
+    st = lib.fa2_bwd_stages(7 | 8, *p, atomic - 1, B, Hq, Hkv, N, 96, 1, 0.125, None)
+    assert st == UNSUPPORTED                       # the head dim is checked before the workspace
+    st = lib.fa2_bwd_stages(7 | 8, *p, atomic - 1, B, Hq, 3, N, d, 1, 0.125, None)
+    assert st == INVALID                           # Hq % Hkv, before any launch
 
 
 def test_aliasing_is_rejected(lib):

@@ -32,11 +32,11 @@ def run_fwd_bwd(qb, kb, vb, dob, causal, scale=None, atomic=False):
     from exact_io_aware_26_amd import fa2
     q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
     o, L = fa2.forward(q, k, v, causal=causal, scale=scale)
-    nbytes = fa2.workspace_bytes(*q.shape[:2], k.shape[1], *q.shape[2:])
+    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
+    nbytes = fa2.workspace_bytes(*q.shape[:2], k.shape[1], *q.shape[2:], stages=stages)
     # Workspace and outputs deliberately full of garbage: the kernels must overwrite them.
     ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=q.device)
     grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
-    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
     dq, dk, dv = fa2.backward(q, k, v, o, L, do, causal=causal, scale=scale, workspace=ws,
                               grads=grads, stages=stages)
     torch.cuda.synchronize()
@@ -89,7 +89,8 @@ def test_bwd_atomic_dq_mode(B, Hq, Hkv, N, d, causal):
 
 
 def head_case(w, heads):
-    """Full-size workload: every element finite; chosen K/V heads against the oracle."""
+    """Full-size workload: every element finite; chosen K/V heads against the oracle at the
+    stated gates (no widening)."""
     log(f"[bwd] workload {w.name} (seed {w.seed}) heads {heads}")
     qb, kb, vb, dob = inputs.attention_inputs(w.seed, w.B, w.Hq, w.Hkv, w.N, w.d, with_grad=True)
     _, _, dq, dk, dv = run_fwd_bwd(qb, kb, vb, dob, w.causal)
@@ -100,11 +101,11 @@ def head_case(w, heads):
     for (b, hk) in heads:
         log(f"[bwd]   oracle head b={b} hk={hk}")
         rdq, rdk, rdv, _, _ = orc.backward_head(q64, k64, v64, do64, b, hk, w.causal, w.scale)
-        wdq, wdk, wdv = orc.backward_bf16_head(q64, k64, v64, do64, b, hk, w.causal, w.scale)
-        parity.check_bf16(f"dQ b{b} hk{hk}", parity.bf16_to_f64(dq[b, hk * G:(hk + 1) * G]), rdq,
-                          working=wdq)
-        parity.check_bf16(f"dK b{b} hk{hk}", parity.bf16_to_f64(dk[b, hk]), rdk, working=wdk)
-        parity.check_bf16(f"dV b{b} hk{hk}", parity.bf16_to_f64(dv[b, hk]), rdv, working=wdv)
+        for name, got, ref in ((f"dQ b{b} hk{hk}", dq[b, hk * G:(hk + 1) * G], rdq),
+                               (f"dK b{b} hk{hk}", dk[b, hk], rdk), (f"dV b{b} hk{hk}", dv[b, hk], rdv)):
+            m = parity.check_bf16(name, parity.bf16_to_f64(got), ref)
+            log(f"[bwd]   {name}: beyond rounding {m['max_abs_beyond_rounding']:.2e}, "
+                f"raw {m['max_abs']:.2e}, rel-L2 {m['rel_l2']:.2e}")
 
 
 def test_bwd_workload_full_size_heads():
@@ -204,7 +205,8 @@ def test_bwd_stages_in_separate_calls_equal_one_call(mode):
     q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
     o, L = fa2.forward(q, k, v, causal=True)
     dq1, dk1, dv1 = fa2.backward(q, k, v, o, L, do, causal=True, stages=fa2.BWD_ALL | mode)
-    ws = torch.empty(fa2.workspace_bytes(1, 4, 2, 1100, 128), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(fa2.workspace_bytes(1, 4, 2, 1100, 128, stages=fa2.BWD_ALL | mode), dtype=torch.uint8,
+                     device=q.device)
     grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
     for st in (fa2.BWD_PREPROCESS, fa2.BWD_MAIN, fa2.BWD_FINALIZE):
         fa2.backward(q, k, v, o, L, do, causal=True, workspace=ws, grads=grads, stages=st | mode)
@@ -244,3 +246,35 @@ def test_fwd_bwd_caller_scale(d, mult):
     tf.full_case(14, 1, 2, 2, 130, d, False, scale=scale)
     full_case(13, 1, 2, 1, 200, d, True, scale=scale)
     full_case(14, 1, 2, 2, 130, d, False, scale=scale)
+
+
+# End to end at a sharper softmax, and one dense random draw: the stated max-abs gate
+# is missed here by the method's own rounding, not by the kernels' arithmetic.  D =
+# rowsum(dO o O) takes O from its bf16 store, and the GPU's and the oracle's
+# working-precision O round to neighbouring bf16 values on different elements (each
+# rounds P against its own running maximum); dQ_i and dK_j then move by
+# scale * P_ij * dD_i * |K_j| (|Q_i|), which grows with P_ij at the dominant key.
+# test_gpu_backward_given.py runs the same shapes from the oracle's O and L, where
+# both sides share one O, under the stated or logged gates.
+KNOWN_LIMITS = [
+    # (seed, B, Hq, Hkv, N, d, causal, multiple of 1/sqrt(d))
+    (1058, 2, 6, 3, 128, 128, False, 1.0),
+    (13, 1, 2, 1, 200, 64, True, 2.0),
+    (13, 1, 2, 1, 200, 64, True, 8.0),
+]
+
+
+@pytest.mark.xfail(reason="end-to-end error dominated by the bf16 store of O entering D "
+                          "(method's own rounding); the backward alone is tested from the "
+                          "oracle's O in test_gpu_backward_given.py", strict=False)
+@pytest.mark.parametrize("seed,B,Hq,Hkv,N,d,causal,mult", KNOWN_LIMITS)
+def test_fwd_bwd_known_limits(seed, B, Hq, Hkv, N, d, causal, mult):
+    scale = mult / math.sqrt(d)
+    log(f"[bwd] known limit: seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} "
+        f"scale={mult}/sqrt(d)")
+    qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True)
+    _, _, dq, dk, dv = run_fwd_bwd(qb, kb, vb, dob, causal, scale)
+    q64, k64, v64, do64 = (inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb, dob))
+    rdq, rdk, rdv, _ = orc.backward(q64, k64, v64, do64, causal, scale)
+    for name, got, ref in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        parity.check_bf16(name, parity.bf16_to_f64(got), ref)

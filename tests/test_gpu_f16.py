@@ -60,10 +60,10 @@ def bwd_case(seed, B, Hq, Hkv, N, d, causal, atomic=False):
     qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True, fmt="f16")
     q, k, v, do = (to_dev(x) for x in (qb, kb, vb, dob))
     o, L = fa2.forward(q, k, v, causal=causal)
-    nbytes = fa2.workspace_bytes(B, Hq, Hkv, N, d)
+    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
+    nbytes = fa2.workspace_bytes(B, Hq, Hkv, N, d, stages=stages)
     ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=q.device)
     grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
-    stages = fa2.BWD_ALL | (fa2.BWD_DQ_ATOMIC if atomic else 0)
     dq, dk, dv = fa2.backward(q, k, v, o, L, do, causal=causal, workspace=ws, grads=grads, stages=stages)
     torch.cuda.synchronize()
     q64, k64, v64, do64 = (inputs.f16_bits_to_f64(x) for x in (qb, kb, vb, dob))
