@@ -51,8 +51,53 @@ def measured_traffic(launches_per_dispatch: float = 1.0):
     return float(t["bytes_per_launch"]) * launches_per_dispatch
 
 
-def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
-    """The fp64 oracle on whole (batch, head) slices of the same inputs until ~budget_s."""
+def _half_ulp_bf16(ref):
+    import numpy as np
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return np.ldexp(1.0, (np.floor(np.log2(a)) - 8).astype(np.int64))
+
+
+class _ParityAccumulator:
+    """Errors of GPU outputs against the fp64 oracle over the sampled heads: raw max-abs,
+    max-abs beyond the output's own bf16 rounding (half an ulp of the exact value), and
+    relative L2 over all sampled elements."""
+
+    def __init__(self):
+        self.acc = {}
+
+    def add(self, name, got, ref):
+        import numpy as np
+        err = np.abs(got - ref)
+        a = self.acc.setdefault(name, {"max_abs": 0.0, "beyond": 0.0, "num": 0.0, "den": 0.0,
+                                       "finite": True})
+        a["max_abs"] = max(a["max_abs"], float(err.max()))
+        a["beyond"] = max(a["beyond"], float(np.maximum(0.0, err - _half_ulp_bf16(ref)).max()))
+        a["num"] += float(np.sum((got - ref) ** 2))
+        a["den"] += float(np.sum(ref ** 2))
+        a["finite"] = a["finite"] and bool(np.all(np.isfinite(got)))
+
+    def report(self, gates):
+        out, ok = {}, True
+        for name, a in self.acc.items():
+            r = {"max_abs": a["max_abs"], "finite": a["finite"]}
+            if name == "L":
+                ok = ok and a["finite"] and a["max_abs"] <= gates["L_max_abs"]
+            else:
+                r["max_abs_beyond_rounding"] = a["beyond"]
+                r["rel_l2"] = (a["num"] / a["den"]) ** 0.5 if a["den"] > 0 else 0.0
+                ok = ok and a["finite"] and r["max_abs_beyond_rounding"] <= gates["max_abs_beyond_rounding"] \
+                    and r["rel_l2"] <= gates["rel_l2"]
+            out[name] = r
+        return out, ok
+
+
+def cpu_baseline(w, qb, kb, vb, dob, budget_s: float, gpu_out=None):
+    """The fp64 oracle on whole (batch, head) slices of the same inputs until ~budget_s.
+
+    gpu_out: optional callable (b, hq) -> dict of the GPU's O, L, dQ (and, with one query
+    head per K/V head, dK, dV) of that head as float64 arrays, from the timed step; the
+    oracle's results of every timed slice are then compared with them (outside the
+    timed region) and the errors returned as the second value."""
     import numpy as np
     from exact_io_aware_26_amd import inputs
     from oracle import oracle as orc
@@ -61,6 +106,7 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
     G = w.Hq // w.Hkv
     heads, flops, t_total = 0, 0.0, 0.0
     per_head_flops = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.Hq)
+    par = _ParityAccumulator()
     while heads < w.B * w.Hq:
         b, hq = divmod(heads, w.Hq)
         hk = hq // G
@@ -69,15 +115,20 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
         v = inputs.bf16_bits_to_f64(vb[b:b + 1, hk:hk + 1])
         do = inputs.bf16_bits_to_f64(dob[b:b + 1, hq:hq + 1])
         t0 = time.perf_counter()
-        orc.forward(q, k, v, w.causal, w.scale, lib=lib)
-        orc.backward(q, k, v, do, w.causal, w.scale, lib=lib)
+        ro, rL = orc.forward(q, k, v, w.causal, w.scale, lib=lib)
+        rdq, rdk, rdv, _ = orc.backward(q, k, v, do, w.causal, w.scale, lib=lib)
         t_total += time.perf_counter() - t0
         flops += per_head_flops
         heads += 1
+        if gpu_out is not None:
+            got = gpu_out(b, hq)
+            ref = {"O": ro[0, 0], "L": rL[0, 0], "dQ": rdq[0, 0], "dK": rdk[0, 0], "dV": rdv[0, 0]}
+            for name, x in got.items():
+                par.add(name, x, ref[name])
         log(f"cpu baseline: {heads} head(s) in {t_total:.1f} s")
         if t_total >= budget_s:
             break
-    return {
+    cpu = {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": orc.num_threads(lib),
@@ -86,7 +137,13 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float):
                    f"[1,1,{w.N},{w.d}] causal of the same inputs, {t_total:.1f} s; "
                    "rate = the slices' FLOPs (same convention) / wall time"),
     }
-
+    if gpu_out is None:
+        return cpu, None
+    gates = {"max_abs_beyond_rounding": 1e-2, "rel_l2": 5e-3, "L_max_abs": 1e-3}
+    errors, ok = par.report(gates)
+    parity = {"against": "fp64 oracle", "sample": f"the {heads} (batch, head) slice(s) timed above, "
+              "outputs of the last timed step", "gates": gates, "pass": ok, "errors": errors}
+    return cpu, parity
 
 
 def _median_ms(torch, fn, warmup=20, groups=5, per_group=10):
@@ -160,6 +217,23 @@ def extra_figures(torch, fa2, workloads, dev):
                      "fwd_ms": fmed, "fwd_ms_min": fmn, "fwd_tflops": ff / (fmed * 1e-3) / 1e12,
                      "bwd_ms": bmed, "bwd_ms_min": bmn, "bwd_tflops": 2.5 * ff / (bmed * 1e-3) / 1e12}
         del q, k, v, do, o, lse, ws, grads, bm
+    # The headline shape's backward with the pages' atomic accumulation of dQ (the
+    # FA2_BWD_DQ_ATOMIC mode: dQ added into an fp32 accumulator inside the K/V loop).
+    wl = workloads.BWD
+    log(f"extra figures: {wl.name} backward, atomic dQ")
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    mk = lambda h: torch.randn(wl.B, h, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+    q, k, v, do = mk(wl.Hq), mk(wl.Hkv), mk(wl.Hkv), mk(wl.Hq)
+    o, lse = fa2.forward(q, k, v, causal=wl.causal)
+    mode = fa2.BWD_ALL | fa2.BWD_DQ_ATOMIC
+    ws = torch.empty(fa2.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d, stages=mode), dtype=torch.uint8,
+                     device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    bmed, bmn = _median_ms(torch, lambda: fa2.backward(q, k, v, o, lse, do, causal=wl.causal, workspace=ws,
+                                                       grads=grads, stages=mode), warmup=5, groups=3, per_group=5)
+    out[wl.name + "_bwd_atomic_dq"] = {"bwd_ms": bmed, "bwd_ms_min": bmn,
+                                       "bwd_tflops": wl.bwd_flops() / (bmed * 1e-3) / 1e12}
+    del q, k, v, do, o, lse, ws, grads
     # The headline shape with f16 inputs and outputs (the fa2_*_f16 entry points).
     wl = workloads.BWD
     log(f"extra figures: {wl.name} in f16")
@@ -297,10 +371,20 @@ def main() -> int:
     if not args.no_extra:
         extra = extra_figures(torch, fa2, workloads, dev)
 
-    cpu = None
+    cpu, parity = None, None
     if args.cpu_budget > 0:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline(w, qb, kb, vb, dob, args.cpu_budget)
+        log("cpu baseline (oracle) and parity of the timed step's outputs")
+        G = w.Hq // w.Hkv
+
+        def gpu_out(b, hq):
+            def f64(t):
+                return inputs.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view("uint16"))
+            out = {"O": f64(o[b, hq]), "L": lse[b, hq].double().cpu().numpy(), "dQ": f64(dq[b, hq])}
+            if G == 1:
+                out.update({"dK": f64(dk[b, hq]), "dV": f64(dv[b, hq])})
+            return out
+
+        cpu, parity = cpu_baseline(w, qb, kb, vb, dob, args.cpu_budget, gpu_out)
 
     line = {
         "metric": METRIC,
@@ -325,6 +409,7 @@ def main() -> int:
         "bwd_stage_ms": {"preprocess_D": pre_ms, "dk_dv_loop": main_ms, "dq_pass": dq_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

@@ -69,7 +69,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 def _log_gate(name: str, m: dict, stated: tuple, applied: tuple) -> None:
     w = m["working_precision"]
-    line = (f"[gate] {name}: beyond-rounding stated {stated[0]:.1e} applied {applied[0]:.2e} "
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    line = (f"[gate] {test} {name}: beyond-rounding stated {stated[0]:.1e} applied {applied[0]:.2e} "
             f"(working precision {w['max_abs_beyond_rounding']:.2e}, measured {m['max_abs_beyond_rounding']:.2e}); "
             f"raw stated {stated[1]:.1e} applied {applied[1]:.2e}; "
             f"rel-L2 stated {stated[2]:.1e} applied {applied[2]:.2e} (measured {m['rel_l2']:.2e})")
