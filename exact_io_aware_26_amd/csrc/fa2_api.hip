@@ -9,9 +9,18 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "fa2.h"
 #include "fa2_kernels.h"
+
+// Scratch of fa2_bwd_noalloc: the backward's per-row arrays (-D and L * log2(e))
+// for callers that cannot allocate.  Each device holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+static constexpr size_t kScratchBytes = FA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -129,7 +138,8 @@ WorkspaceLayout workspace_layout(uint64_t rows_pad, uint64_t q_elems, bool atomi
 fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                         const void* dO, const void* dQ, const void* dK, const void* dV,
                         const void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
-                        float scale, bool atomic, bool* empty, Sizes* sz) {
+                        float scale, bool atomic, bool* empty, Sizes* sz,
+                        bool static_ws = false) {
     fa2_status s = check_problem(B, Hq, Hkv, N, d, scale, empty, sz);
     if (s != FA2_OK || *empty) return s;
     const void* ptrs[9] = {Q, K, V, O, L, dO, dQ, dK, dV};
@@ -138,22 +148,26 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
         if (!ptrs[i]) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
         if (!aligned16(ptrs[i])) return fail(FA2_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
     }
-    if (!ws) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is NULL");
-    if ((reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) != 0)
-        return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     const WorkspaceLayout wl = workspace_layout(sz->rows_pad, sz->q_elems, atomic);
-    if (ws_bytes < wl.total) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace too small");
+    // static_ws: the library's own scratch array, checked by the caller of this
+    // function against its fixed size; only the caller's buffers are checked here.
+    if (!static_ws) {
+        if (!ws) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is NULL");
+        if ((reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) != 0)
+            return fail(FA2_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+        if (ws_bytes < wl.total) return fail(FA2_ERR_INVALID_ARGUMENT, "workspace too small");
+    }
     const uint64_t qb = sz->q_elems * 2, kb = sz->kv_elems * 2, lb = sz->rows * 4;
     const void* ins[6] = {Q, K, V, O, L, dO};
     const uint64_t in_bytes[6] = {qb, kb, kb, qb, lb, qb};
     const void* outs[4] = {dQ, dK, dV, ws};
-    const uint64_t out_bytes[4] = {qb, kb, kb, wl.total};
+    const uint64_t out_bytes[4] = {qb, kb, kb, static_ws ? 0 : wl.total};
     const char* out_names[4] = {"dQ", "dK", "dV", "workspace"};
-    for (int o = 0; o < 4; ++o) {
+    for (int o = 0; o < (static_ws ? 3 : 4); ++o) {
         for (int i = 0; i < 6; ++i)
             if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i]))
                 return fail(FA2_ERR_INVALID_ARGUMENT, "%s aliases an input", out_names[o]);
-        for (int o2 = o + 1; o2 < 4; ++o2)
+        for (int o2 = o + 1; o2 < (static_ws ? 3 : 4); ++o2)
             if (overlaps(outs[o], out_bytes[o], outs[o2], out_bytes[o2]))
                 return fail(FA2_ERR_INVALID_ARGUMENT, "%s aliases another output", out_names[o]);
     }
@@ -176,6 +190,29 @@ fa2_status validate_mask(const unsigned char* bmask, int N, int d, const void* c
 }
 
 constexpr double kLog2e = 1.4426950408889634074;
+
+// Device address of `scratch` on each device, looked up on the first
+// fa2_bwd_noalloc call made with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa2_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA2_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA2_ERR_UNSUPPORTED, "device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FA2_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA2_OK;
+}
 
 }  // namespace
 
@@ -370,6 +407,30 @@ fa2_status fa2_bwd_stages_f16(unsigned stages, const void* Q, const void* K, con
                               int Hkv, int N, int d, int causal, float scale, void* stream) {
     return bwd_impl(true, stages, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq,
                     Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                           const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
+                           int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    Sizes sz;
+    fa2_status s = validate_bwd(Q, K, V, O, L, dO, dQ, dK, dV, nullptr, 0, B, Hq, Hkv, N, d, scale,
+                                false, &empty, &sz, /*static_ws=*/true);
+    if (s != FA2_OK || empty) return s;
+    const size_t need = workspace_layout(sz.rows_pad, sz.q_elems, false).total;
+    if (need > kScratchBytes) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "problem needs %zu bytes of scratch; the static scratch holds %zu "
+                      "(B * Hq * N rounded up to 64 rows per head must stay within %zu rows)",
+                      need, kScratchBytes, kScratchBytes / 8);
+        return FA2_ERR_UNSUPPORTED;
+    }
+    void* ws = nullptr;
+    s = scratch_for_current_device(&ws);
+    if (s != FA2_OK) return s;
+    return bwd_impl(false, FA2_BWD_ALL, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, ws,
+                    kScratchBytes, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
 fa2_status fa2_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* L,

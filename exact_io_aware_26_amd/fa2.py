@@ -25,10 +25,11 @@ FA2_ERR_HIP = 3
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
            "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes",
            "fa2_bwd_stages_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
-           "fa2_last_error")
+           "fa2_last_error", "fa2_bwd_noalloc")
 DTYPES = (torch.bfloat16, torch.float16)
 
 BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
+NOALLOC_SCRATCH_BYTES = 16 << 20      # fa2_bwd_noalloc's static scratch per GPU
 SPARSE_BLOCK = 128            # query rows and keys per block-sparse mask block
 SPARSE_MAX_N = 262144
 
@@ -58,6 +59,8 @@ def load(path: str | None = None):
     lib.fa2_bwd.restype = i
     lib.fa2_bwd_stages.argtypes = [ctypes.c_uint] + lib.fa2_bwd.argtypes
     lib.fa2_bwd_stages.restype = i
+    lib.fa2_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_noalloc.restype = i
     for name, like in (("fa2_fwd_f16", lib.fa2_fwd), ("fa2_bwd_f16", lib.fa2_bwd),
                        ("fa2_bwd_stages_f16", lib.fa2_bwd_stages)):
         fn = getattr(lib, name)
@@ -226,6 +229,26 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
              B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    _check(st, lib)
+    return dq, dk, dv
+
+
+def backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, do: torch.Tensor, grads, causal: bool = False,
+                     scale: float | None = None):
+    """The bf16 backward through fa2_bwd_noalloc: no workspace, nothing allocated by the
+    library or here; the caller passes the outputs ``grads=(dq, dk, dv)``.  Calls on
+    one GPU share its static scratch and must not overlap in time."""
+    lib = load()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("fa2_bwd_noalloc takes bfloat16 tensors")
+    B, Hq, Hkv, N, d = check_backward_args(q, k, v, o, lse, do, None, grads)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = grads
+    st = lib.fa2_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                             _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv
 

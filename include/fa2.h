@@ -45,7 +45,8 @@
  * before anything is launched (nothing is written then); a launch failure
  * returns FA2_ERR_HIP; a fault inside a kernel surfaces at the caller's next
  * synchronization with the stream, not as a return value.  The library is
- * thread-safe (no mutable global state beyond a per-thread error message).
+ * thread-safe (no mutable global state beyond a per-thread error message and
+ * the per-device address of fa2_bwd_noalloc's static scratch).
  *
  * Determinism: the forward pass and fa2_bwd are bitwise reproducible.  The
  * optional atomic-dQ mode of fa2_bwd_stages sums dQ with fp32 atomics and is
@@ -153,6 +154,28 @@ fa2_status fa2_bwd_stages(unsigned stages, const void *Q, const void *K, const v
                           const void *O, const float *L, const void *dO, void *dQ, void *dK,
                           void *dV, void *workspace, size_t workspace_bytes, int B, int Hq,
                           int Hkv, int N, int d, int causal, float scale, void *stream);
+
+/*
+ * fa2_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments (minus the workspace), layouts,
+ * checks, kernels, results (bitwise those of fa2_bwd) and errors as fa2_bwd.
+ * The per-row scratch (-D and L * log2(e), 8 bytes per query row, rows padded
+ * to 64 per head) lives in a static device array of FA2_NOALLOC_SCRATCH_BYTES
+ * bytes that each GPU holds until the process ends; its address is looked up
+ * on the first call made with that device current (the device the stream
+ * belongs to).  The call allocates nothing.  A problem needing more than the
+ * array (B * Hq * round_up(N, 64) above FA2_NOALLOC_SCRATCH_BYTES / 8 rows)
+ * returns FA2_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two streams,
+ * or two threads) race on it and must be ordered by the caller.  The array
+ * needs no clearing between calls: each call writes every entry it reads.
+ */
+#define FA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa2_status fa2_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O,
+                           const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                           void *stream);
 
 /*
  * FP16 inputs and outputs (the pages' problem statement allows FP16 or BF16).

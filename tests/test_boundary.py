@@ -245,3 +245,24 @@ def test_block_sparse_entry_points_check_the_mask_before_any_hip_call(lib):
     assert bwd(*p, p[6] + 16, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID   # inside dQ
     assert bwd(*p, ws + 512, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID    # inside the workspace
     assert bwd(*p, addr(10), ws, nbytes - 1, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
+
+
+def test_noalloc_backward_checks_before_any_hip_call(lib):
+    """fa2_bwd_noalloc: the same argument checks as fa2_bwd (no workspace), and problems
+    whose per-row scratch exceeds the static array are refused, all before any HIP call."""
+    p = [addr(i) for i in range(9)]
+    noalloc = lib.fa2_bwd_noalloc
+    assert noalloc(*p, 0, 4, 2, 100, 128, 1, 0.125, None) == OK            # empty problem
+    assert noalloc(*p, 2, 6, 4, 100, 128, 1, 0.125, None) == INVALID       # Hq % Hkv
+    assert noalloc(*p, 2, 4, 2, 100, 96, 1, 0.125, None) == UNSUPPORTED    # head dim
+    q = list(p)
+    q[6] = q[0]                                                            # dQ = Q
+    assert noalloc(*q, 2, 4, 2, 100, 128, 1, 0.125, None) == INVALID
+    q = list(p)
+    q[2] = None
+    assert noalloc(*q, 2, 4, 2, 100, 128, 1, 0.125, None) == INVALID
+    # 8 bytes per padded row: 2^21 rows fit 16 MiB, one more 64-row head does not.
+    max_rows = fa2.NOALLOC_SCRATCH_BYTES // 8
+    assert noalloc(*p, 1, 1, 1, max_rows + 64, 64, 1, 0.125, None) == UNSUPPORTED
+    assert b"scratch" in lib.fa2_last_error()
+    assert noalloc(*p, 1, 33, 1, 65536, 64, 1, 0.125, None) == UNSUPPORTED
