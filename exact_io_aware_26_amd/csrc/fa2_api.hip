@@ -218,8 +218,8 @@ fa2_status scratch_for_current_device(void** out) {
 
 extern "C" {
 
-const char* fa2_status_string(fa2_status s) {
-    switch (s) {
+const char* fa2_status_string(int status) {
+    switch (status) {
         case FA2_OK: return "FA2_OK";
         case FA2_ERR_INVALID_ARGUMENT: return "FA2_ERR_INVALID_ARGUMENT";
         case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED";

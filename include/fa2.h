@@ -243,8 +243,9 @@ fa2_status fa2_validate_bwd(const void *Q, const void *K, const void *V, const v
                             size_t workspace_bytes, int B, int Hq, int Hkv, int N,
                             int d, int causal, float scale);
 
-/* Static, human-readable name of a status code ("unknown status" otherwise). */
-const char *fa2_status_string(fa2_status s);
+/* Static, human-readable name of a status code: any int, so that a value that
+ * is not an fa2_status (e.g. from a newer library) gives "unknown status". */
+const char *fa2_status_string(int status);
 
 /*
  * Detail of the last non-OK status returned on the calling thread (which
