@@ -175,12 +175,11 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
 }
 
 // Block-sparse attention: the block mask [nb, nb] bytes, nb = ceil(N / 128).
-// It must be present, d must be 64 or 128, N at most kSparseMaxN (the kernels
-// hold one mask row or column of tiles in LDS), and no output may overlap it.
-fa2_status validate_mask(const unsigned char* bmask, int N, int d, const void* const* outs,
+// It must be present, N at most kSparseMaxN (the kernels hold one mask row or
+// column of tiles in LDS), and no output may overlap it.
+fa2_status validate_mask(const unsigned char* bmask, int N, const void* const* outs,
                          const uint64_t* out_bytes, int n_outs) {
     if (!bmask) return fail(FA2_ERR_INVALID_ARGUMENT, "block_mask is NULL");
-    if (d != 64 && d != 128) return fail(FA2_ERR_UNSUPPORTED, "block-sparse attention needs d = 64 or 128");
     if (N > fa2::kSparseMaxN) return fail(FA2_ERR_UNSUPPORTED, "block-sparse attention needs N <= 262144");
     const uint64_t nb = (uint64_t)((N + fa2::kSparseBlock - 1) / fa2::kSparseBlock);
     for (int o = 0; o < n_outs; ++o)
@@ -286,7 +285,7 @@ fa2_status fwd_impl(bool f16, bool sparse, const unsigned char* bmask, const voi
     if (sparse) {
         const void* outs[2] = {O, L};
         const uint64_t ob[2] = {sz.q_elems * 2, sz.rows * 4};
-        s = validate_mask(bmask, N, d, outs, ob, 2);
+        s = validate_mask(bmask, N, outs, ob, 2);
         if (s != FA2_OK) return s;
     }
     fa2::FwdParams p;
@@ -330,7 +329,7 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
     if (sparse) {
         const void* outs[4] = {dQ, dK, dV, workspace};
         const uint64_t ob[4] = {sz.q_elems * 2, sz.kv_elems * 2, sz.kv_elems * 2, wl.total};
-        s = validate_mask(bmask, N, d, outs, ob, 4);
+        s = validate_mask(bmask, N, outs, ob, 4);
         if (s != FA2_OK) return s;
     }
     fa2::BwdParams p;
@@ -445,6 +444,21 @@ fa2_status fa2_bwd_block_sparse(const void* Q, const void* K, const void* V, con
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                                 int causal, float scale, void* stream) {
     return bwd_impl(false, FA2_BWD_ALL, true, block_mask, Q, K, V, O, L, dO, dQ, dK, dV, workspace,
+                    workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_fwd_block_sparse_f16(const void* Q, const void* K, const void* V, void* O, float* L,
+                                    const unsigned char* block_mask, int B, int Hq, int Hkv, int N,
+                                    int d, int causal, float scale, void* stream) {
+    return fwd_impl(true, true, block_mask, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_bwd_block_sparse_f16(const void* Q, const void* K, const void* V, const void* O,
+                                    const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                                    const unsigned char* block_mask, void* workspace,
+                                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                    int causal, float scale, void* stream) {
+    return bwd_impl(true, FA2_BWD_ALL, true, block_mask, Q, K, V, O, L, dO, dQ, dK, dV, workspace,
                     workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 

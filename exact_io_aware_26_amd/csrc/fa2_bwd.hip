@@ -1074,7 +1074,10 @@ void bwd_dq_pipe_kernel(const BwdParams p) {
 // the same program as bwd_dq_pipe's: the s, dp products of block s alternate
 // with the dQ products of block s - 2, while the dS of block s - 1 is formed
 // beside them.  The dQ^T accumulators and the Q / dO operands fill the AGPRs.
-template <bool CAUSAL>
+// Block-sparse (SPARSE): a workgroup is one 128-row mask block and walks the
+// 32-key tiles of the key blocks its mask row keeps (causal: at or below the
+// diagonal) from an LDS list.
+template <bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq256_kernel(const BwdParams p) {
     constexpr int D = 256;
@@ -1137,11 +1140,35 @@ void bwd_dq256_kernel(const BwdParams p) {
         dq_d[u] = q < N ? -p.Dneg[row] : 0.f;
     }
 
-    const int n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
+    // 32-key tiles of the walk (one block per tile).  Block-sparse: the list
+    // entries, the tiles of every key block the workgroup's mask block needs.
+    int n_kb;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(BRQ == kSparseBlock && kSparseBlock % BT == 0, "one mask block per workgroup");
+        __shared__ uint16_t tl_arr[kSparseMaxN / BT];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int r0 = q0 / kSparseBlock, nb = p.nb;
+            const int n = build_block_tiles<kSparseBlock / BT>(tl, nb, (N + BT - 1) / BT, lane, [&](int c) {
+                return p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0);
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_kb = __builtin_amdgcn_readfirstlane(tl_count);
+    } else {
+        n_kb = CAUSAL ? (min(q0 + BRQ, N) - 1) / 32 + 1 : (N + 31) / 32;
+    }
     const int n_t = n_kb;
+    auto tile_at = [&](int t) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl[t]);
+        else return t;
+    };
 
     auto copy_part = [&](int t, int buf, int j) {
-        const int kv0 = min(t, n_t - 1) * BT;
+        const int kv0 = tile_at(min(t, n_t - 1)) * BT;
         const int last = N - 1 - kv0;
         const int i = j % PERW;
         const int R = (wave * PERW + i) * RPI;
@@ -1258,7 +1285,8 @@ void bwd_dq256_kernel(const BwdParams p) {
             }
         };
         {
-            const int kb0 = 32 * (s - 1);
+            // Block s - 1 (stages past the last block compute scores nobody reads).
+            const int kb0 = SPARSE ? tile_at(min(max(s - 1, 0), n_kb - 1)) * BT : 32 * (s - 1);
             if ((CAUSAL && kb0 + 31 > wq0) || kb0 + 32 > N) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -1302,6 +1330,8 @@ void bwd_dq256_kernel(const BwdParams p) {
         barrier_lds();
     };
 
+    // A block-sparse workgroup with no tile only writes dQ = 0.
+    if (!SPARSE || n_kb > 0) {
     // Prologue: tile 0; the buffers of tiles -2 and -1 zeroed.
     for (int i = tid; i < 2 * kTile / 16; i += 64 * NW) {
         lds_store16(Kbuf + 2 * kTile + 16 * i, u32x4{0, 0, 0, 0});
@@ -1319,6 +1349,7 @@ void bwd_dq256_kernel(const BwdParams p) {
         if (s + 3 < n_stage) stage(std::integral_constant<int, 3>{}, s + 3);
     }
     wait_vm_all();
+    }
     // The accumulators were last written by matrix products issued from inline
     // assembly, which the compiler does not track: wait them out before reading.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1713,7 +1744,7 @@ void bwd_kv_kernel(const BwdParams p) {
 // of the columns.  That costs the s and dp products twice, but the whole K/V
 // rows and 128 columns of both accumulators (held in AGPRs) fit one wave's
 // registers.  64-row query tiles (Q, dO: 32 KiB each) are copied two deep.
-template <bool CAUSAL>
+template <bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_kv256_kernel(const BwdParams p) {
     constexpr int D = 256, DH = 128;          // head dim; dK / dV columns per workgroup
@@ -1775,11 +1806,37 @@ void bwd_kv256_kernel(const BwdParams p) {
     }
 
     // Query tiles: for each of the G query heads sharing this K/V head, the
-    // 64-row tiles from the first one the causal mask lets through.
+    // 64-row tiles from the first one the causal mask lets through.  Block-
+    // sparse: the key tile is one mask column; the tiles of the query blocks
+    // whose mask byte in it is set (causal: at or below the diagonal), from an
+    // LDS list built by wave 0 (each of the pair's workgroups builds its own).
     const int n_qt = (N + BR - 1) / BR;
     const int i_begin = CAUSAL ? kv0 / BR : 0;
-    const int n_i = n_qt - i_begin;
+    int n_i;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(BC == kSparseBlock && kSparseBlock % BR == 0, "one mask column per key tile");
+        __shared__ uint16_t tl_arr[kSparseMaxN / BR];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int nb = p.nb;
+            const int n = build_block_tiles<kSparseBlock / BR>(tl, nb, n_qt, lane, [&](int r) {
+                return p.bmask[(size_t)r * nb + kvtile] != 0 && (!CAUSAL || r >= kvtile);
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_i = __builtin_amdgcn_readfirstlane(tl_count);
+    } else {
+        n_i = n_qt - i_begin;
+    }
     const int n_iter = n_i * p.G;
+    // First row of query tile i of the walk.
+    auto qrow_at = [&](int i) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl[i]) * BR;
+        else return (i_begin + i) * BR;
+    };
 
     // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
     // tile program spreads over its first slots: Q and dO rows
@@ -1797,7 +1854,7 @@ void bwd_kv256_kernel(const BwdParams p) {
     };
     auto plan_copy = [&](int it, FA2_LDS char* T) {
         const int hq = hk * p.G + it / n_i;
-        const int qt0 = (i_begin + it % n_i) * BR;
+        const int qt0 = qrow_at(it % n_i);
         const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
         const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
         TileCopy c;
@@ -2002,7 +2059,7 @@ void bwd_kv256_kernel(const BwdParams p) {
     auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
         // The other buffer was released by the barrier ending the previous
         // step.  Copies past the last tile repeat it into it (never read).
-        tile(T, (i_begin + it % n_i) * BR, plan_copy(min(it + 1, n_iter - 1), Tw));
+        tile(T, qrow_at(it % n_i), plan_copy(min(it + 1, n_iter - 1), Tw));
         wait_vm_all();                  // tile it+1 has landed
         barrier_lds();
     };
@@ -2062,7 +2119,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
     const long rows = (long)p.B * p.Hq * p.N;
     const long rows_pad = (long)p.B * p.Hq * p.Npad;
     const bool atomic_dq = (stages & 8u) != 0;
-    if (p.bmask && (D > 128 || atomic_dq)) return hipErrorInvalidValue;   // block-sparse: d <= 128, dQ pass
+    if (p.bmask && atomic_dq) return hipErrorInvalidValue;   // block-sparse: dQ in its own pass
     if (stages & 1u) {
         constexpr int RPB = 256 / (D / 8);
         long rows_arg = rows_pad;
@@ -2093,7 +2150,8 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
             grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
             threads = 64 * BwdCfg<D>::NW;
         } else {
-            fn = reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL>);
+            fn = p.bmask ? reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL, true>)
+                         : reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL, false>);
             grid = 2L * p.B * p.Hkv * ((p.N + 127) / 128);       // two column halves per key tile
             threads = 256;
         }
@@ -2114,7 +2172,8 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
         if constexpr (D <= 128)
             fn = p.bmask ? reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL, true>)
                          : reinterpret_cast<const void*>(&bwd_dq_pipe_kernel<D, CAUSAL, false>);
-        else fn = reinterpret_cast<const void*>(&bwd_dq256_kernel<CAUSAL>);
+        else fn = p.bmask ? reinterpret_cast<const void*>(&bwd_dq256_kernel<CAUSAL, true>)
+                          : reinterpret_cast<const void*>(&bwd_dq256_kernel<CAUSAL, false>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, stream);
     }
     return hipSuccess;

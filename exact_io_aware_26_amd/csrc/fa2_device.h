@@ -168,6 +168,32 @@ __device__ __forceinline__ int build_tile_list(FA2_LDS uint16_t* list, int n_blk
     return single ? count - 1 : count;   // the single-tile block is the last entry
 }
 
+// Block-sparse tile list without flags, built by one wave: for the blocks
+// c < n_blk whose pred(c) holds, in increasing c, the tiles TPB*c ..
+// TPB*c + TPB - 1 that lie below n_tiles (only the last block can be short).
+// Returns the number of entries (wave-uniform).  Tile indices fit 16 bits.
+template <int TPB, typename Pred>
+__device__ __forceinline__ int build_block_tiles(FA2_LDS uint16_t* list, int n_blk, int n_tiles, int lane,
+                                                 Pred pred) {
+    int count = 0, short_by = 0;
+    for (int c0 = 0; c0 < n_blk; c0 += 64) {
+        const int c = c0 + lane;
+        const bool f = c < n_blk && pred(c);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (f) {
+            const int pos = count + TPB * (int)below;
+#pragma unroll
+            for (int t = 0; t < TPB; ++t)
+                if (TPB * c + t < n_tiles) list[pos + t] = (uint16_t)(TPB * c + t);
+        }
+        if (__builtin_amdgcn_ballot_w64(f && TPB * c + TPB > n_tiles) != 0) short_by = TPB * n_blk - n_tiles;
+        count += TPB * __builtin_popcountll(m);
+    }
+    return count - short_by;
+}
+
 // 16-byte LDS load / store.
 __device__ __forceinline__ u32x4 lds_load16(const FA2_LDS char* p) {
     return *reinterpret_cast<const FA2_LDS u32x4*>(p);

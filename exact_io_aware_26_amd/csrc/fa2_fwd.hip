@@ -505,7 +505,11 @@ void fwd_pipe_kernel(const FwdParams p) {
 // step, and 4 waves (one per SIMD, 128 rows per workgroup: the O~ accumulator
 // alone takes 128 registers).  With one wave per SIMD nothing else hides a
 // wave's latencies, so each step is issued as fixed slot programs (below).
-template <bool CAUSAL>
+// Block-sparse (SPARSE): a workgroup is exactly one 128-row mask block, so it
+// streams the 32-key tiles of the key blocks its mask row keeps (causal: at
+// or below the diagonal) from an LDS list and runs the dense step program on
+// them; a workgroup whose list is empty writes O = 0 and L = -inf.
+template <bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_pipe256_kernel(const FwdParams p) {
     constexpr int D = 256;
@@ -559,9 +563,40 @@ void fwd_pipe256_kernel(const FwdParams p) {
         qf[ks] = as_el8(v);
     }
 
-    // Tiles the workgroup streams, and tiles this wave computes on.
-    const int n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
-    const int n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+    // Tiles the workgroup streams, and tiles this wave computes on (block-
+    // sparse: entries of the list, up to this wave's causal limit).
+    int n_kv, n_w;
+    FA2_LDS uint16_t* tl = nullptr;
+    if constexpr (SPARSE) {
+        static_assert(ROWS == kSparseBlock && kSparseBlock % BC == 0, "one mask block per workgroup");
+        constexpr int TPB = kSparseBlock / BC;
+        __shared__ uint16_t tl_arr[kSparseMaxN / BC];
+        __shared__ int tl_count;
+        tl = (FA2_LDS uint16_t*)tl_arr;
+        if (wave == 0) {
+            const int r0 = q0 / kSparseBlock, nb = p.nb;
+            const int n = build_block_tiles<TPB>(tl, nb, (N + BC - 1) / BC, lane, [&](int c) {
+                return p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0);
+            });
+            if (lane == 0) tl_count = n;
+        }
+        __syncthreads();
+        n_kv = __builtin_amdgcn_readfirstlane(tl_count);
+        n_w = wq0 >= N ? 0 : n_kv;
+        if (CAUSAL) {
+            const int t_last = min(wq0 + 31, N - 1) / BC;
+            while (n_w > 0 && (int)tl[n_w - 1] > t_last) --n_w;
+            n_w = __builtin_amdgcn_readfirstlane(n_w);
+        }
+    } else {
+        n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
+        n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
+    }
+    // Key tile of step j.
+    auto tile_at = [&](int j) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl[j]);
+        else return j;
+    };
 
     // Copy tile t of K or V into LDS.  Lane i of a copy instruction writes
     // bytes 16*i.. of its 1 KiB (tile row R + i / CPR, 16-byte slot i % CPR),
@@ -614,8 +649,8 @@ void fwd_pipe256_kernel(const FwdParams p) {
             }
     };
 
-    auto mask = [&](int t, f32x16 (&s)[NBS]) {
-        const int kv0 = t * BC;
+    auto mask = [&](int j, f32x16 (&s)[NBS]) {
+        const int kv0 = tile_at(j) * BC;
         if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
             // As in fwd_pipe_kernel: masked when the constant key offset exceeds lim.
             const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - kv0 - 4 * g;
@@ -633,14 +668,16 @@ void fwd_pipe256_kernel(const FwdParams p) {
     float m_run = kNegInf;   // reference max of c * S (log2 domain), equal in lanes l and l ^ 32
     float l_run = 0.f;       // this lane's half of the row sum, relative to m_run
 
+    // A block-sparse workgroup may have no tile at all: it only writes O = 0, L = -inf.
+    if (!SPARSE || n_kv > 0) {
     // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
-    copy_tile(Kh, 0, K0);
-    copy_tile(Vh, 0, V0);
+    copy_tile(Kh, tile_at(0), K0);
+    copy_tile(Vh, tile_at(0), V0);
     if (1 < n_kv) {
-        copy_tile(Kh, 1, K1);
-        copy_tile(Vh, 1, V1);
+        copy_tile(Kh, tile_at(1), K1);
+        copy_tile(Vh, tile_at(1), V1);
     }
-    if (2 < n_kv) copy_tile(Kh, 2, K2);
+    if (2 < n_kv) copy_tile(Kh, tile_at(2), K2);
     wait_vm_all();
     __syncthreads();
     f32x16 sa[NBS], sb[NBS];       // scores of the current and the next tile, alternating
@@ -701,7 +738,9 @@ void fwd_pipe256_kernel(const FwdParams p) {
                 const float m_new = mx > m_run + kLazyMax ? mx : m_run;
                 alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
                 m_run = m_new;
-                m_sub = m_new;
+                // Block-sparse rows may not have met an unmasked key yet (m = -inf):
+                // exp2(-inf - 0) = 0 then, where -inf - (-inf) would be NaN.
+                m_sub = SPARSE && m_new == kNegInf ? 0.f : m_new;
                 pin(m_sub);
                 pin(alpha);
             } else if (ks < 13) {
@@ -747,8 +786,8 @@ void fwd_pipe256_kernel(const FwdParams p) {
                     f32x16 (&s_cur)[NBS], f32x16 (&s_next)[NBS]) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        copy_tile(Kh, min(j + 3, n_kv - 1), Kw);
-        copy_tile(Vh, min(j + 2, n_kv - 1), Vw);
+        copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
+        copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
         if (j < n_w) {
             mask(j, s_cur);
             uint32_t pp[8];
@@ -779,11 +818,13 @@ void fwd_pipe256_kernel(const FwdParams p) {
         if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
     }
     wait_vm_all();
+    }
 
-    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l)
-    if (n_w > 0) {
+    // ---- epilogue: O = O~ / l, L = ln2 * (m + log2 l); a block-sparse row
+    // without any unmasked key has l = 0: O = 0 and L = -inf.
+    if (SPARSE ? wq0 < N : n_w > 0) {
         const float l_tot = sum_halves(l_run);
-        const float inv = 1.0f / l_tot;
+        const float inv = SPARSE && !(l_tot > 0.f) ? 0.f : 1.0f / l_tot;
         if (q < N) {
             uint16_t* Orow = p.O + qhead + (size_t)q * D;
 #pragma unroll
@@ -796,7 +837,9 @@ void fwd_pipe256_kernel(const FwdParams p) {
                     w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + d0) = w;
                 }
-            if (g == 0) p.L[((size_t)b * p.Hq + hq) * N + q] = (m_run + log2f(l_tot)) * kLn2;
+            if (g == 0)
+                p.L[((size_t)b * p.Hq + hq) * N + q] =
+                    SPARSE && !(l_tot > 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
         }
     }
 }
@@ -812,11 +855,11 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
                                  : reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512), args, 0, stream);
     } else {
-        if (p.bmask) return hipErrorInvalidValue;   // block-sparse: d <= 128 only
         arg.n_qtiles = (p.N + 127) / 128;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
-        return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pipe256_kernel<CAUSAL>),
-                               dim3((unsigned)grid), dim3(256), args, 0, stream);
+        const void* fn = p.bmask ? reinterpret_cast<const void*>(&fwd_pipe256_kernel<CAUSAL, true>)
+                                 : reinterpret_cast<const void*>(&fwd_pipe256_kernel<CAUSAL, false>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, stream);
     }
 }
 

@@ -25,7 +25,7 @@ FA2_ERR_HIP = 3
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
            "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes",
            "fa2_bwd_stages_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
-           "fa2_last_error", "fa2_bwd_noalloc")
+           "fa2_last_error", "fa2_bwd_noalloc", "fa2_fwd_block_sparse_f16", "fa2_bwd_block_sparse_f16")
 DTYPES = (torch.bfloat16, torch.float16)
 
 BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
@@ -71,6 +71,11 @@ def load(path: str | None = None):
     lib.fa2_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          i, i, i, i, i, i, f, vp]
     lib.fa2_bwd_block_sparse.restype = i
+    for name, like in (("fa2_fwd_block_sparse_f16", lib.fa2_fwd_block_sparse),
+                       ("fa2_bwd_block_sparse_f16", lib.fa2_bwd_block_sparse)):
+        fn = getattr(lib, name)
+        fn.argtypes = like.argtypes
+        fn.restype = i
     lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_bwd_workspace_bytes.restype = sz
     lib.fa2_bwd_stages_workspace_bytes.argtypes = [ctypes.c_uint, i, i, i, i, i]
@@ -270,15 +275,14 @@ def _block_mask(block_mask: torch.Tensor, N: int, device) -> torch.Tensor:
 def forward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
                          causal: bool = False, scale: float | None = None,
                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Block-sparse forward (bf16): scores of 128 x 128 blocks whose mask byte is 0 are masked.
+    """Block-sparse forward (bf16 or f16): scores of 128 x 128 blocks whose mask byte is 0
+    are masked.
 
     block_mask [ceil(N/128), ceil(N/128)] uint8 or bool on q's device, shared by every
     batch and head.  Rows with no unmasked key get o = 0 and lse = -inf.
     """
     lib = load()
     B, Hq, Hkv, N, d = check_forward_args(q, k, v, out, lse)
-    if q.dtype != torch.bfloat16:
-        raise TypeError("block-sparse attention takes bfloat16 tensors")
     bm = _block_mask(block_mask, N, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -286,8 +290,9 @@ def forward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = lib.fa2_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(bm),
-                                  B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    fwd = lib.fa2_fwd_block_sparse_f16 if q.dtype == torch.float16 else lib.fa2_fwd_block_sparse
+    st = fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(bm),
+             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return out, lse
 
@@ -299,8 +304,6 @@ def backward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
     """Gradients of the block-sparse forward (same mask; o, lse from forward_block_sparse)."""
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
-    if q.dtype != torch.bfloat16:
-        raise TypeError("block-sparse attention takes bfloat16 tensors")
     bm = _block_mask(block_mask, N, q.device)
     nbytes = lib.fa2_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     check_backward_args(q, k, v, o, lse, do, workspace, grads, nbytes)
@@ -310,9 +313,10 @@ def backward_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
                                                   torch.empty_like(v))
-    st = lib.fa2_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(bm), _ptr(workspace),
-                                  workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)),
-                                  float(scale), _stream_handle(q))
+    bwd = lib.fa2_bwd_block_sparse_f16 if q.dtype == torch.float16 else lib.fa2_bwd_block_sparse
+    st = bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(bm), _ptr(workspace),
+             workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)),
+             float(scale), _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv

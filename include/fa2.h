@@ -208,16 +208,17 @@ fa2_status fa2_bwd_stages_f16(unsigned stages, const void *Q, const void *K, con
  *   (r, c) masks the scores of query rows 128r..128r+127 against keys
  *   128c..128c+127 (set to -inf before the softmax, as the causal mask does;
  *   both apply when causal != 0).  Masked blocks cost no matrix products in
- *   the K/V-tile loop of the backward; the forward and the dQ pass run
- *   workgroups of 256 query rows, which compute the key tiles either of
- *   their two mask rows needs.
+ *   the K/V-tile loop of the backward, nor, at d = 256, anywhere; at d = 64
+ *   and 128 the forward and the dQ pass run workgroups of 256 query rows,
+ *   which compute the key tiles either of their two mask rows needs.
  *   A query row with no unmasked score gets O = 0 and L = -inf; its dQ is 0
  *   and it adds nothing to dK or dV.
- * Same layouts, workspace, outputs and errors as fa2_fwd / fa2_bwd (bf16),
- * plus FA2_ERR_INVALID_ARGUMENT for a NULL block_mask (with work) or an
- * output overlapping it, and FA2_ERR_UNSUPPORTED for d = 256 or N above
+ * Same layouts, workspace, outputs and errors as fa2_fwd / fa2_bwd, for every
+ * head dim (64, 128, 256), plus FA2_ERR_INVALID_ARGUMENT for a NULL block_mask
+ * (with work) or an output overlapping it, and FA2_ERR_UNSUPPORTED for N above
  * FA2_SPARSE_MAX_N.  fa2_bwd_block_sparse takes the forward's O and L of the
  * same mask; it always computes dQ in its own pass (bitwise reproducible).
+ * The _f16 variants take IEEE binary16 tensors, as fa2_fwd_f16 / fa2_bwd_f16.
  */
 #define FA2_SPARSE_BLOCK 128
 #define FA2_SPARSE_MAX_N 262144
@@ -229,6 +230,14 @@ fa2_status fa2_bwd_block_sparse(const void *Q, const void *K, const void *V, con
                                 const unsigned char *block_mask, void *workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                                 int causal, float scale, void *stream);
+fa2_status fa2_fwd_block_sparse_f16(const void *Q, const void *K, const void *V, void *O, float *L,
+                                    const unsigned char *block_mask, int B, int Hq, int Hkv, int N,
+                                    int d, int causal, float scale, void *stream);
+fa2_status fa2_bwd_block_sparse_f16(const void *Q, const void *K, const void *V, const void *O,
+                                    const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                                    const unsigned char *block_mask, void *workspace,
+                                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                    int causal, float scale, void *stream);
 
 /*
  * The argument checks of fa2_fwd / fa2_bwd alone: no HIP call is made, so

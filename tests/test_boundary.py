@@ -226,9 +226,12 @@ def test_block_sparse_entry_points_check_the_mask_before_any_hip_call(lib):
     # NULL mask with work; an empty problem needs none.
     assert fwd(q, k, v, o, L, None, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
     assert fwd(None, None, None, None, None, None, 2, 4, 2, 0, 128, 1, 0.1, None) == OK
-    # Head dims and sizes the block-sparse kernels do not cover.
-    assert fwd(q, k, v, o, L, mask, 2, 4, 2, 300, 256, 1, 0.1, None) == UNSUPPORTED
+    # Sizes the block-sparse kernels do not cover (every head dim is covered; a NULL
+    # mask is refused at d = 256 too).
+    assert fwd(q, k, v, o, L, None, 2, 4, 2, 300, 256, 1, 0.1, None) == INVALID
+    assert fwd(q, k, v, o, L, mask, 2, 4, 2, 300, 96, 1, 0.1, None) == UNSUPPORTED
     assert fwd(q, k, v, o, L, mask, 1, 1, 1, fa2.SPARSE_MAX_N + 1, 64, 1, 0.1, None) == UNSUPPORTED
+    assert lib.fa2_fwd_block_sparse_f16(q, k, v, o, L, None, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
     # An output overlapping the mask (mask inside O, and inside L).
     assert fwd(q, k, v, o, L, o + 64, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
     assert fwd(q, k, v, o, L, L + 8, 2, 4, 2, 300, 128, 0, 0.1, None) == INVALID
@@ -241,7 +244,9 @@ def test_block_sparse_entry_points_check_the_mask_before_any_hip_call(lib):
     assert bwd(*p, None, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID
     assert "block_mask" in lib.fa2_last_error().decode()
     nbytes256 = ws_bytes(lib, 2, 4, 2, 300, 256)
-    assert bwd(*p, addr(10), ws, nbytes256, 2, 4, 2, 300, 256, 1, 0.1, None) == UNSUPPORTED
+    assert bwd(*p, None, ws, nbytes256, 2, 4, 2, 300, 256, 1, 0.1, None) == INVALID
+    assert lib.fa2_bwd_block_sparse_f16(*p, addr(10), ws, nbytes256 - 1, 2, 4, 2, 300, 256, 1, 0.1,
+                                        None) == INVALID
     assert bwd(*p, p[6] + 16, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID   # inside dQ
     assert bwd(*p, ws + 512, ws, nbytes, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID    # inside the workspace
     assert bwd(*p, addr(10), ws, nbytes - 1, 2, 4, 2, 300, 128, 1, 0.1, None) == INVALID

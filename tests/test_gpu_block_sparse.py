@@ -1,4 +1,5 @@
-"""Block-sparse attention on the GPU against the fp64 oracle with the same block mask.
+"""Block-sparse attention on the GPU against the fp64 oracle with the same block mask
+(every head dim; bf16 and f16).
 
 The mask (one byte per 128 x 128 block, shared by all batches and heads)
 masks scores like the causal mask does; rows the mask leaves without any key
@@ -29,9 +30,19 @@ def _gpu():
     fa2.load()
 
 
-def run(qb, kb, vb, dob, mask, causal, scale=None):
+def to_dev(bits, fmt):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if fmt == "bf16" else torch.float16).to("cuda")
+
+
+def to_f64(t):
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return inputs.bf16_bits_to_f64(bits) if t.dtype == torch.bfloat16 else inputs.f16_bits_to_f64(bits)
+
+
+def run(qb, kb, vb, dob, mask, causal, scale=None, fmt="bf16"):
     from exact_io_aware_26_amd import fa2
-    q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
+    q, k, v, do = (to_dev(x, fmt) for x in (qb, kb, vb, dob))
     bm = torch.from_numpy(mask).to(q.device)
     out = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
@@ -45,16 +56,17 @@ def run(qb, kb, vb, dob, mask, causal, scale=None):
     return o, L, dq, dk, dv
 
 
-def check_case(seed, B, Hq, Hkv, N, d, causal, kind, backward=True):
+def check_case(seed, B, Hq, Hkv, N, d, causal, kind, backward=True, fmt="bf16"):
     mask = inputs.block_mask(kind, N, seed=seed)
     log(f"[sparse] seed={seed} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} mask={kind} "
-        f"({int(mask.sum())}/{mask.size} blocks)")
-    qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True)
-    o, L, dq, dk, dv = run(qb, kb, vb, dob, mask, causal)
-    q64, k64, v64, do64 = (inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb, dob))
+        f"({int(mask.sum())}/{mask.size} blocks) {fmt}")
+    qb, kb, vb, dob = inputs.attention_inputs(seed, B, Hq, Hkv, N, d, with_grad=True, fmt=fmt)
+    o, L, dq, dk, dv = run(qb, kb, vb, dob, mask, causal, fmt=fmt)
+    widen = inputs.bf16_bits_to_f64 if fmt == "bf16" else inputs.f16_bits_to_f64
+    q64, k64, v64, do64 = (widen(x) for x in (qb, kb, vb, dob))
     sc = 1.0 / math.sqrt(d)
     ro, rL = orc.forward(q64, k64, v64, causal, sc, block_mask=mask)
-    go, gL = parity.bf16_to_f64(o), parity.f32_to_f64(L)
+    go, gL = to_f64(o), parity.f32_to_f64(L)
     empty = np.isneginf(rL)
     # Rows without any key: exactly O = 0 and L = -inf.
     assert np.array_equal(np.isneginf(gL), empty), "rows with L = -inf differ from the oracle's"
@@ -64,18 +76,24 @@ def check_case(seed, B, Hq, Hkv, N, d, causal, kind, backward=True):
     if not backward:
         return
     rdq, rdk, rdv, _ = orc.backward(q64, k64, v64, do64, causal, sc, block_mask=mask)
-    wdq, wdk, wdv = orc.backward_bf16(q64, k64, v64, do64, causal, sc, block_mask=mask)
-    gdq = parity.bf16_to_f64(dq)
+    gdq = to_f64(dq)
     assert np.all(gdq[empty] == 0.0), "dQ of rows without any key must be 0"
+    if fmt == "f16":
+        # The f16 path: stated gates (no working-precision widening).
+        parity.check_bf16("dQ (f16)", gdq, rdq)
+        parity.check_bf16("dK (f16)", to_f64(dk), rdk)
+        parity.check_bf16("dV (f16)", to_f64(dv), rdv)
+        return
+    wdq, wdk, wdv = orc.backward_bf16(q64, k64, v64, do64, causal, sc, block_mask=mask)
     parity.check_bf16("dQ", gdq, rdq, working=wdq)
-    parity.check_bf16("dK", parity.bf16_to_f64(dk), rdk, working=wdk)
-    parity.check_bf16("dV", parity.bf16_to_f64(dv), rdv, working=wdv)
+    parity.check_bf16("dK", to_f64(dk), rdk, working=wdk)
+    parity.check_bf16("dV", to_f64(dv), rdv, working=wdv)
 
 
 KINDS = ("random", "local_global", "diagonal", "column0", "strided", "ones", "zeros")
 CASES = []
 for i, N in enumerate((1, 100, 128, 129, 255, 300, 513, 700)):
-    for d in (64, 128):
+    for d in (64, 128, 256):
         for causal in (False, True):
             kind = KINDS[(i + d // 64 + causal) % len(KINDS)]
             heads = [(1, 1), (4, 2), (2, 2), (4, 1)][(i + causal) % 4]
@@ -93,7 +111,24 @@ def test_block_sparse_mask_kinds(kind, causal):
     check_case(21, 1, 2, 1, 1100, 128, causal, kind)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_mask_kinds_d256(kind, causal):
+    check_case(22, 1, 4, 2, 1100, 256, causal, kind)
+
+
+F16_CASES = [(1, 2, 1, 300, 64, True, "random"), (2, 4, 2, 700, 128, False, "local_global"),
+             (1, 4, 1, 1100, 128, True, "strided"), (1, 2, 2, 513, 256, True, "random"),
+             (1, 2, 1, 1024, 256, False, "diagonal"), (1, 2, 1, 129, 64, False, "zeros")]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,kind", F16_CASES)
+def test_block_sparse_f16(B, Hq, Hkv, N, d, causal, kind):
+    """The binary16 entry points (fa2_fwd_block_sparse_f16, fa2_bwd_block_sparse_f16)."""
+    check_case(600 + N + d, B, Hq, Hkv, N, d, causal, kind, fmt="f16")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_random_multi_tile(d, causal):
     # Random masks differ between the two 128-row mask blocks of a 256-row
@@ -104,12 +139,14 @@ def test_block_sparse_random_multi_tile(d, causal):
 
 def test_block_sparse_all_ones_is_dense_bitwise():
     from exact_io_aware_26_amd import fa2
-    for (N, d, causal) in ((1000, 128, True), (777, 64, False), (2048, 128, False), (300, 64, True)):
-        log(f"[sparse] all-ones vs dense N={N} d={d} causal={causal}")
-        qb, kb, vb, dob = inputs.attention_inputs(77 + N, 2, 4, 2, N, d, with_grad=True)
+    for (N, d, causal, fmt) in ((1000, 128, True, "bf16"), (777, 64, False, "bf16"), (2048, 128, False, "bf16"),
+                                (300, 64, True, "bf16"), (1000, 256, True, "bf16"), (333, 256, False, "bf16"),
+                                (700, 128, True, "f16"), (515, 256, False, "f16")):
+        log(f"[sparse] all-ones vs dense N={N} d={d} causal={causal} {fmt}")
+        qb, kb, vb, dob = inputs.attention_inputs(77 + N, 2, 4, 2, N, d, with_grad=True, fmt=fmt)
         mask = inputs.block_mask("ones", N)
-        o, L, dq, dk, dv = run(qb, kb, vb, dob, mask, causal)
-        q, k, v, do = (parity.to_device_bf16(x) for x in (qb, kb, vb, dob))
+        o, L, dq, dk, dv = run(qb, kb, vb, dob, mask, causal, fmt=fmt)
+        q, k, v, do = (to_dev(x, fmt) for x in (qb, kb, vb, dob))
         o2, L2 = fa2.forward(q, k, v, causal=causal)
         dq2, dk2, dv2 = fa2.backward(q, k, v, o2, L2, do, causal=causal)
         torch.cuda.synchronize()
@@ -144,12 +181,12 @@ def test_block_sparse_large_sampled_rows():
     del fa2
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_block_sparse_maximum_n(d):
     """N = 262144 (the largest block-sparse N: 4096 tiles of 64 keys, the top of
-    the tile lists' 12-bit index) with a local + global mask: sampled rows of O
-    and L against the oracle, including rows of the last block; every
-    gradient element written and finite."""
+    the tile lists' 12-bit index; at d = 256, 8192 tiles of 32 keys) with a
+    local + global mask: sampled rows of O and L against the oracle, including
+    rows of the last block; every gradient element written and finite."""
     from exact_io_aware_26_amd import fa2
     B, Hq, Hkv, N = 1, 1, 1, fa2.SPARSE_MAX_N
     mask = inputs.block_mask("local_global", N)
