@@ -198,21 +198,22 @@ def extra_figures(torch, fa2, workloads, dev):
     # (non-causal).  FLOPs count only the kept blocks.
     from exact_io_aware_26_amd import inputs
     wl = workloads.BWD
-    for kind, causal, name in (("local_global", True, "block_sparse_local_global_causal_b4_h16_n8192_d128"),
-                               ("random", False, "block_sparse_random25_b4_h16_n8192_d128")):
+    for kind, causal, d, name in (("local_global", True, 128, "block_sparse_local_global_causal_b4_h16_n8192_d128"),
+                                  ("random", False, 128, "block_sparse_random25_b4_h16_n8192_d128"),
+                                  ("random", False, 256, "block_sparse_random25_b4_h16_n8192_d256")):
         log(f"extra figures: {name}")
         mask_np = inputs.block_mask(kind, wl.N, seed=wl.seed, density=0.25)
         bm = torch.from_numpy(mask_np).to(dev)
         g = torch.Generator(device=dev).manual_seed(wl.seed)
-        mk = lambda h: torch.randn(wl.B, h, wl.N, wl.d, device=dev, dtype=torch.bfloat16, generator=g)
+        mk = lambda h: torch.randn(wl.B, h, wl.N, d, device=dev, dtype=torch.bfloat16, generator=g)
         q, k, v, do = mk(wl.Hq), mk(wl.Hkv), mk(wl.Hkv), mk(wl.Hq)
         o, lse = fa2.forward_block_sparse(q, k, v, bm, causal=causal)
         fmed, fmn = _median_ms(torch, lambda: fa2.forward_block_sparse(q, k, v, bm, causal=causal, out=o, lse=lse))
-        ws = torch.empty(fa2.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d), dtype=torch.uint8, device=dev)
+        ws = torch.empty(fa2.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.N, d), dtype=torch.uint8, device=dev)
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         bmed, bmn = _median_ms(torch, lambda: fa2.backward_block_sparse(q, k, v, o, lse, do, bm, causal=causal,
                                                                         workspace=ws, grads=grads))
-        ff = workloads.block_sparse_fwd_flops(mask_np, wl.B, wl.Hq, wl.N, wl.d, causal)
+        ff = workloads.block_sparse_fwd_flops(mask_np, wl.B, wl.Hq, wl.N, d, causal)
         out[name] = {"kept_blocks": int(mask_np.sum()), "blocks": int(mask_np.size),
                      "fwd_ms": fmed, "fwd_ms_min": fmn, "fwd_tflops": ff / (fmed * 1e-3) / 1e12,
                      "bwd_ms": bmed, "bwd_ms_min": bmn, "bwd_tflops": 2.5 * ff / (bmed * 1e-3) / 1e12}

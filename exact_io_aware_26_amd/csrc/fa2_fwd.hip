@@ -347,16 +347,18 @@ void fwd_pipe_kernel(const FwdParams p) {
         copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
         copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
         if (j < n_w) {
-            // Block-sparse: a tile this wave's mask block does not need gets
-            // only the products S_{j+1} (they keep the pipeline's shape).
+            // Block-sparse: no work on a tile this wave's mask block does not
+            // need, neither its softmax and P V products (step j) nor its
+            // scores (computed one step ahead, in step j - 1).
             const bool own = !SPARSE || own_at(j);
+            const bool own_next = !SPARSE || (j + 1 < n_w && own_at(j + 1));
             if (own) mask(j, s_cur);
             uint32_t pp[2][8];
             // Raised priority while this wave interleaves S_{j+1} with the
             // softmax of S_j, normal for the P V products: the other wave on the
             // SIMD then fills the matrix unit's idle slots of the mixed phase.
             __builtin_amdgcn_s_setprio(1);
-            scores(Ks, s_next);
+            if (own_next) scores(Ks, s_next);
             if (own) {
                 const float alpha = softmax(s_cur, pp);
                 // Materialize P here, beside the S_{j+1} products, rather than
