@@ -49,6 +49,8 @@
 //     transposed reads.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "fa2_device.h"
 #include "fa2_kernels.h"
 
@@ -1420,9 +1422,19 @@ void bwd_kv_kernel(const BwdParams p) {
     const int g = lane >> 5;
     const int li = lane & 31;
 
+    // Persistent workgroups: items (key tile, batch, K/V head) in order of
+    // decreasing work (causal: the first key tiles have the most query tiles),
+    // dealt to the workgroups in rounds, every other round in reverse order,
+    // so that the work per workgroup evens out.
     const int BHk = p.B * p.Hkv;
-    const int kvtile = blockIdx.x / BHk;
-    const int bh = blockIdx.x - kvtile * BHk;
+    const int n_items = ((p.N + BC - 1) / BC) * BHk;
+    for (int round = 0;; ++round) {
+    const int slot = (round & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int item = round * (int)gridDim.x + slot;
+    if (item >= n_items) break;
+    if (round > 0) __syncthreads();        // the previous item's LDS reads are done
+    const int kvtile = item / BHk;
+    const int bh = item - kvtile * BHk;
     const int b = bh / p.Hkv;
     const int hk = bh - b * p.Hkv;
     const int N = p.N;
@@ -1733,6 +1745,7 @@ void bwd_kv_kernel(const BwdParams p) {
                     u32x2{pack_el(dk[db][4 * rq] * p.scale, dk[db][4 * rq + 1] * p.scale),
                           pack_el(dk[db][4 * rq + 2] * p.scale, dk[db][4 * rq + 3] * p.scale)};
             }
+    }
     }
 }
 
@@ -2113,6 +2126,20 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const BwdParams p, 
     *reinterpret_cast<u32x4*>(p.dQ + i * 8) = out;
 }
 
+// Workgroups of a persistent launch: per_cu resident workgroups on every
+// compute unit of the current device (the count is read once per device).
+long persistent_workgroups(int per_cu) {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256L * per_cu;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return (long)cus[dev] * per_cu;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream) {
     BwdParams arg = p;
@@ -2144,6 +2171,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 threads = 256;
             }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
+            if (!atomic_dq) grid = std::min<long>(grid, persistent_workgroups(1));
         } else if (atomic_dq) {
             fn = reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>);
             constexpr int BC = BwdCfg<D>::BC;
