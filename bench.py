@@ -94,8 +94,9 @@ class _ParityAccumulator:
 def cpu_baseline(w, qb, kb, vb, dob, budget_s: float, gpu_out=None):
     """The fp64 oracle on whole (batch, head) slices of the same inputs until ~budget_s.
 
-    gpu_out: optional callable (b, hq) -> dict of the GPU's O, L, dQ (and, with one query
-    head per K/V head, dK, dV) of that head as float64 arrays, from the timed step; the
+    gpu_out: optional callable (b, hq) -> {"split_o": ..., "plain_o": ...}, each a dict of
+    the GPU's outputs of that head as float64 arrays (the timed step's O, L, dQ and, with
+    one query head per K/V head, dK, dV; the plain-O backward's dQ, dK, dV); the
     oracle's results of every timed slice are then compared with them (outside the
     timed region) and the errors returned as the second value."""
     import numpy as np
@@ -106,7 +107,7 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float, gpu_out=None):
     G = w.Hq // w.Hkv
     heads, flops, t_total = 0, 0.0, 0.0
     per_head_flops = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.Hq)
-    par = _ParityAccumulator()
+    par, par_plain = _ParityAccumulator(), _ParityAccumulator()
     while heads < w.B * w.Hq:
         b, hq = divmod(heads, w.Hq)
         hk = hq // G
@@ -123,8 +124,10 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float, gpu_out=None):
         if gpu_out is not None:
             got = gpu_out(b, hq)
             ref = {"O": ro[0, 0], "L": rL[0, 0], "dQ": rdq[0, 0], "dK": rdk[0, 0], "dV": rdv[0, 0]}
-            for name, x in got.items():
+            for name, x in got["split_o"].items():
                 par.add(name, x, ref[name])
+            for name, x in got["plain_o"].items():
+                par_plain.add(name, x, ref[name])
         log(f"cpu baseline: {heads} head(s) in {t_total:.1f} s")
         if t_total >= budget_s:
             break
@@ -141,8 +144,12 @@ def cpu_baseline(w, qb, kb, vb, dob, budget_s: float, gpu_out=None):
         return cpu, None
     gates = {"max_abs_beyond_rounding": 1e-2, "rel_l2": 5e-3, "L_max_abs": 1e-3}
     errors, ok = par.report(gates)
+    errors_plain, ok_plain = par_plain.report(gates)
     parity = {"against": "fp64 oracle", "sample": f"the {heads} (batch, head) slice(s) timed above, "
-              "outputs of the last timed step", "gates": gates, "pass": ok, "errors": errors}
+              "outputs of the last timed step (split O: D from O + O_lo)", "gates": gates, "pass": ok,
+              "errors": errors,
+              "plain_o": {"sample": "the same slices through fa2_bwd (D from the bf16 O alone)",
+                          "pass": ok_plain, "errors": errors_plain}}
     return cpu, parity
 
 
@@ -289,16 +296,20 @@ def main() -> int:
 
     q, k, v, do = (to_dev(x) for x in (qb, kb, vb, dob))
     o = torch.empty_like(q)
+    o_lo = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa2.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
     grads = (dq, dk, dv)
 
+    # The step: the forward with O's rounding residual (fa2_fwd_olo) and the
+    # backward forming D from O + O_lo (fa2_bwd_stages_olo).
     def fwd():
-        fa2.forward(q, k, v, causal=w.causal, out=o, lse=lse)
+        fa2.forward(q, k, v, causal=w.causal, out=o, lse=lse, o_lo=o_lo)
 
     def bwd(stages):
-        fa2.backward(q, k, v, o, lse, do, causal=w.causal, workspace=ws, grads=grads, stages=stages)
+        fa2.backward(q, k, v, o, lse, do, causal=w.causal, workspace=ws, grads=grads, stages=stages,
+                     o_lo=o_lo)
 
     if args.probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -368,9 +379,25 @@ def main() -> int:
         "algorithmic_flops_per_launch": main_flops,
     }
 
+    # The same step without the residual (fa2_fwd, fa2_bwd: D from the bf16 O), timed
+    # as the extra figures are, its outputs kept for the parity record.
+    log("plain-O step: fa2_fwd and fa2_bwd")
+    grads_plain = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    pf_med, _ = _median_ms(torch, lambda: fa2.forward(q, k, v, causal=w.causal, out=o, lse=lse),
+                           warmup=5, groups=3, per_group=10)
+    pb_med, _ = _median_ms(torch, lambda: fa2.backward(q, k, v, o, lse, do, causal=w.causal, workspace=ws,
+                                                       grads=grads_plain), warmup=5, groups=3, per_group=5)
+    sf_med, _ = _median_ms(torch, fwd, warmup=5, groups=3, per_group=10)
+    sb_med, _ = _median_ms(torch, lambda: bwd(fa2.BWD_ALL), warmup=5, groups=3, per_group=5)
+    torch.cuda.synchronize()
+    plain = {"fwd_ms": pf_med, "fwd_tflops": fwd_f / (pf_med * 1e-3) / 1e12,
+             "bwd_ms": pb_med, "bwd_tflops": bwd_f / (pb_med * 1e-3) / 1e12,
+             "split_o_fwd_ms": sf_med, "split_o_bwd_ms": sb_med}
+
     extra = {}
     if not args.no_extra:
         extra = extra_figures(torch, fa2, workloads, dev)
+    extra[w.name + "_plain_o"] = plain
 
     cpu, parity = None, None
     if args.cpu_budget > 0:
@@ -381,9 +408,11 @@ def main() -> int:
             def f64(t):
                 return inputs.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view("uint16"))
             out = {"O": f64(o[b, hq]), "L": lse[b, hq].double().cpu().numpy(), "dQ": f64(dq[b, hq])}
+            plain_out = {"dQ": f64(grads_plain[0][b, hq])}
             if G == 1:
                 out.update({"dK": f64(dk[b, hq]), "dV": f64(dv[b, hq])})
-            return out
+                plain_out.update({"dK": f64(grads_plain[1][b, hq]), "dV": f64(grads_plain[2][b, hq])})
+            return {"split_o": out, "plain_o": plain_out}
 
         cpu, parity = cpu_baseline(w, qb, kb, vb, dob, args.cpu_budget, gpu_out)
 
@@ -401,7 +430,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "scale": w.scale, "seed": w.seed},
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "entry_points": "fa2_fwd_olo + fa2_bwd_stages_olo (split O)"},
         "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,

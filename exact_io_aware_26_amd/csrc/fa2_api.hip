@@ -174,6 +174,18 @@ fa2_status validate_bwd(const void* Q, const void* K, const void* V, const void*
     return FA2_OK;
 }
 
+// O_lo of the split-O entry points: present, 16-byte aligned, and (in the
+// forward, where it is an output) not overlapping the inputs.  The forward
+// also checks it against O and L, the backward against its outputs.
+fa2_status validate_olo(const void* Olo, const void* Q, const void* K, const void* V, const Sizes& sz) {
+    if (!Olo) return fail(FA2_ERR_INVALID_ARGUMENT, "O_lo is NULL");
+    if (!aligned16(Olo)) return fail(FA2_ERR_INVALID_ARGUMENT, "O_lo is not 16-byte aligned");
+    const uint64_t qb = sz.q_elems * 2, kb = sz.kv_elems * 2;
+    if (overlaps(Olo, qb, Q, qb) || overlaps(Olo, qb, K, kb) || overlaps(Olo, qb, V, kb))
+        return fail(FA2_ERR_INVALID_ARGUMENT, "O_lo aliases Q, K or V");
+    return FA2_OK;
+}
+
 // Block-sparse attention: the block mask [nb, nb] bytes, nb = ceil(N / 128).
 // It must be present, N at most kSparseMaxN (the kernels hold one mask row or
 // column of tiles in LDS), and no output may overlap it.
@@ -276,12 +288,18 @@ namespace {
 // block-sparse entry point (which then requires a mask).
 fa2_status fwd_impl(bool f16, bool sparse, const unsigned char* bmask, const void* Q, const void* K,
                     const void* V, void* O, float* L, int B, int Hq, int Hkv, int N, int d,
-                    int causal, float scale, void* stream) {
+                    int causal, float scale, void* stream, bool with_olo = false, void* Olo = nullptr) {
     g_last_error[0] = '\0';
     bool empty;
     Sizes sz;
     fa2_status s = validate_fwd(Q, K, V, O, L, B, Hq, Hkv, N, d, scale, &empty, &sz);
     if (s != FA2_OK || empty) return s;
+    if (with_olo) {
+        s = validate_olo(Olo, Q, K, V, sz);
+        if (s != FA2_OK) return s;
+        if (overlaps(Olo, sz.q_elems * 2, O, sz.q_elems * 2) || overlaps(Olo, sz.q_elems * 2, L, sz.rows * 4))
+            return fail(FA2_ERR_INVALID_ARGUMENT, "O_lo aliases another output");
+    }
     if (sparse) {
         const void* outs[2] = {O, L};
         const uint64_t ob[2] = {sz.q_elems * 2, sz.rows * 4};
@@ -293,6 +311,7 @@ fa2_status fwd_impl(bool f16, bool sparse, const unsigned char* bmask, const voi
     p.K = static_cast<const uint16_t*>(K);
     p.V = static_cast<const uint16_t*>(V);
     p.O = static_cast<uint16_t*>(O);
+    p.Olo = static_cast<uint16_t*>(Olo);
     p.L = L;
     p.B = B;
     p.Hq = Hq;
@@ -314,7 +333,7 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
                     const void* Q, const void* K, const void* V, const void* O, const float* L,
                     const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                     size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
-                    float scale, void* stream) {
+                    float scale, void* stream, bool with_olo = false, const void* Olo = nullptr) {
     g_last_error[0] = '\0';
     if ((stages & FA2_BWD_ALL) == 0 || (stages & ~(FA2_BWD_ALL | FA2_BWD_DQ_ATOMIC)) != 0)
         return fail(FA2_ERR_INVALID_ARGUMENT,
@@ -326,6 +345,15 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
                                 Hkv, N, d, scale, atomic, &empty, &sz);
     if (s != FA2_OK || empty) return s;
     const WorkspaceLayout wl = workspace_layout(sz.rows_pad, sz.q_elems, atomic);
+    if (with_olo) {
+        s = validate_olo(Olo, Q, K, V, sz);
+        if (s != FA2_OK) return s;
+        const void* outs[4] = {dQ, dK, dV, workspace};
+        const uint64_t ob[4] = {sz.q_elems * 2, sz.kv_elems * 2, sz.kv_elems * 2, wl.total};
+        for (int o = 0; o < 4; ++o)
+            if (overlaps(outs[o], ob[o], Olo, sz.q_elems * 2))
+                return fail(FA2_ERR_INVALID_ARGUMENT, "an output aliases O_lo");
+    }
     if (sparse) {
         const void* outs[4] = {dQ, dK, dV, workspace};
         const uint64_t ob[4] = {sz.q_elems * 2, sz.kv_elems * 2, sz.kv_elems * 2, wl.total};
@@ -337,6 +365,7 @@ fa2_status bwd_impl(bool f16, unsigned stages, bool sparse, const unsigned char*
     p.K = static_cast<const uint16_t*>(K);
     p.V = static_cast<const uint16_t*>(V);
     p.O = static_cast<const uint16_t*>(O);
+    p.Olo = static_cast<const uint16_t*>(Olo);
     p.L = L;
     p.dO = static_cast<const uint16_t*>(dO);
     p.dQ = static_cast<uint16_t*>(dQ);
@@ -430,6 +459,29 @@ fa2_status fa2_bwd_noalloc(const void* Q, const void* K, const void* V, const vo
     if (s != FA2_OK) return s;
     return bwd_impl(false, FA2_BWD_ALL, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, ws,
                     kScratchBytes, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa2_status fa2_fwd_olo(const void* Q, const void* K, const void* V, void* O, void* O_lo, float* L,
+                       int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* stream) {
+    return fwd_impl(false, false, nullptr, Q, K, V, O, L, B, Hq, Hkv, N, d, causal, scale, stream,
+                    true, O_lo);
+}
+
+fa2_status fa2_bwd_olo(const void* Q, const void* K, const void* V, const void* O, const void* O_lo,
+                       const float* L, const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                       size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                       float scale, void* stream) {
+    return bwd_impl(false, FA2_BWD_ALL, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace,
+                    workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream, true, O_lo);
+}
+
+fa2_status fa2_bwd_stages_olo(unsigned stages, const void* Q, const void* K, const void* V,
+                              const void* O, const void* O_lo, const float* L, const void* dO,
+                              void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              void* stream) {
+    return bwd_impl(false, stages, false, nullptr, Q, K, V, O, L, dO, dQ, dK, dV, workspace,
+                    workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream, true, O_lo);
 }
 
 fa2_status fa2_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* L,

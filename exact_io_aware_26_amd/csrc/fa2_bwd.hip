@@ -106,7 +106,8 @@ template <int D> struct BwdCfg;
 template <> struct BwdCfg<256> { static constexpr int BC = 64, NW = 2, BR = 32; static constexpr bool KV_REGS = false; };
 
 // ---------------------------------------------------------------------------------------------
-// bwd_pre: per padded row of each head, D_i = sum_d dO_id * O_id (fp32) and
+// bwd_pre: per padded row of each head, D_i = sum_d dO_id * O_id (fp32; with
+// Olo, O_id + Olo_id, the forward's fp32 output to about 16 bits) and
 // L_i * log2(e); rows past N get D = 0 and +inf (so P = 0 there), and so do
 // rows whose L is -inf (block-sparse rows without an unmasked key).  Zeroes the
 // dQ accumulator row when dQ is accumulated with atomics.
@@ -125,11 +126,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p, long ro
         const size_t off = (size_t)row * D + part * 8;
         const u32x4 a = global_load16(p.dO + off);
         const u32x4 b = global_load16(p.O + off);
+        const u32x4 r = p.Olo ? global_load16(p.Olo + off) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t x = a[i], y = b[i];
-            acc = fmaf(lo_el_f32(x), lo_el_f32(y), acc);
-            acc = fmaf(hi_el_f32(x), hi_el_f32(y), acc);
+            const uint32_t x = a[i], y = b[i], z = r[i];
+            acc = fmaf(lo_el_f32(x), lo_el_f32(y) + lo_el_f32(z), acc);
+            acc = fmaf(hi_el_f32(x), hi_el_f32(y) + hi_el_f32(z), acc);
         }
         if (zero_dq) {
             float* z = p.dQacc + off;

@@ -57,6 +57,31 @@ template <int D> __device__ __forceinline__ int swz(int row) {
     return D == 64 ? 4 * ((row >> 1) & 1) + ((row >> 2) & 3) : 4 * (row & 3) + ((row >> 2) & 3);
 }
 
+// Row of O from this lane's fp32 accumulators (the lane's 4 * NBD columns of
+// one query row) scaled by inv, stored as bf16.  With Olo, each element's
+// rounding residual x - bf16(x) (exact in fp32) is stored too, rounded to
+// bf16: O + Olo then carries the fp32 value to about 16 significant bits,
+// from which the backward forms D = rowsum(dO o O) without the 8-bit error of
+// the stored O.
+template <int NBD>
+__device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, const f32x16 (&o)[NBD],
+                                            float inv, int g) {
+#pragma unroll
+    for (int db = 0; db < NBD; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = 32 * db + 8 * rq + 4 * g;
+            const float x0 = o[db][4 * rq] * inv, x1 = o[db][4 * rq + 1] * inv;
+            const float x2 = o[db][4 * rq + 2] * inv, x3 = o[db][4 * rq + 3] * inv;
+            const uint32_t w0 = pack_el(x0, x1), w1 = pack_el(x2, x3);
+            *reinterpret_cast<u32x2*>(Orow + d0) = u32x2{w0, w1};
+            if (Olorow)
+                *reinterpret_cast<u32x2*>(Olorow + d0) =
+                    u32x2{pack_el(x0 - lo_el_f32(w0), x1 - hi_el_f32(w0)),
+                          pack_el(x2 - lo_el_f32(w1), x3 - hi_el_f32(w1))};
+        }
+}
+
 // Pipelined forward for d = 64 and 128: one workgroup = 8 wave64s = 256 query
 // rows (two waves per SIMD), so each K/V tile brought into LDS serves twice
 // as many rows as a 4-wave workgroup would.
@@ -484,17 +509,8 @@ void fwd_pipe_kernel(const FwdParams p) {
         const float l_tot = sum_halves(l_run);
         const float inv = SPARSE && !(l_tot > 0.f) ? 0.f : 1.0f / l_tot;
         if (q < N) {
-            uint16_t* Orow = p.O + qhead + (size_t)q * D;
-#pragma unroll
-            for (int db = 0; db < NBD; ++db)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int d0 = 32 * db + 8 * rq + 4 * g;
-                    u32x2 w;
-                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
-                }
+            store_o_row<NBD>(p.O + qhead + (size_t)q * D, p.Olo ? p.Olo + qhead + (size_t)q * D : nullptr,
+                             o, inv, g);
             if (g == 0)
                 p.L[((size_t)b * p.Hq + hq) * N + q] =
                     SPARSE && !(l_tot > 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
@@ -828,17 +844,8 @@ void fwd_pipe256_kernel(const FwdParams p) {
         const float l_tot = sum_halves(l_run);
         const float inv = SPARSE && !(l_tot > 0.f) ? 0.f : 1.0f / l_tot;
         if (q < N) {
-            uint16_t* Orow = p.O + qhead + (size_t)q * D;
-#pragma unroll
-            for (int db = 0; db < NBD; ++db)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int d0 = 32 * db + 8 * rq + 4 * g;
-                    u32x2 w;
-                    w[0] = pack_el(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-                    w[1] = pack_el(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Orow + d0) = w;
-                }
+            store_o_row<NBD>(p.O + qhead + (size_t)q * D, p.Olo ? p.Olo + qhead + (size_t)q * D : nullptr,
+                             o, inv, g);
             if (g == 0)
                 p.L[((size_t)b * p.Hq + hq) * N + q] =
                     SPARSE && !(l_tot > 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;

@@ -17,6 +17,7 @@ struct FwdParams {
     const uint16_t* K;  // bf16 [B, Hkv, N, D]
     const uint16_t* V;  // bf16 [B, Hkv, N, D]
     uint16_t* O;        // bf16 [B, Hq, N, D]
+    uint16_t* Olo;      // bf16 [B, Hq, N, D]: O's rounding residual (NULL: not written)
     float* L;           // fp32 [B, Hq, N]
     int B, Hq, Hkv, N, G;
     int n_qtiles;       // ceil(N / rows per workgroup)
@@ -30,12 +31,13 @@ struct BwdParams {
     const uint16_t* K;
     const uint16_t* V;
     const uint16_t* O;
+    const uint16_t* Olo;  // O's rounding residual, added to O in D (NULL: D from O alone)
     const float* L;
     const uint16_t* dO;
     uint16_t* dQ;
     uint16_t* dK;
     uint16_t* dV;
-    float* Dneg;   // fp32 [B, Hq, Npad]  workspace: -D = -rowsum(dO o O); 0 past N
+    float* Dneg;   // fp32 [B, Hq, Npad]  workspace: -D = -rowsum(dO o (O + Olo)); 0 past N
     float* L2;     // fp32 [B, Hq, Npad]  workspace: L * log2(e); +inf past N (P = 0 there)
     float* dQacc;  // fp32 [B, Hq, N, D]  workspace: dQ accumulated with atomics
     int B, Hq, Hkv, N, G;

@@ -25,7 +25,8 @@ FA2_ERR_HIP = 3
 EXPORTS = ("fa2_fwd", "fa2_bwd", "fa2_bwd_stages", "fa2_fwd_f16", "fa2_bwd_f16", "fa2_bwd_stages_f16",
            "fa2_fwd_block_sparse", "fa2_bwd_block_sparse", "fa2_bwd_workspace_bytes",
            "fa2_bwd_stages_workspace_bytes", "fa2_validate_fwd", "fa2_validate_bwd", "fa2_status_string",
-           "fa2_last_error", "fa2_bwd_noalloc", "fa2_fwd_block_sparse_f16", "fa2_bwd_block_sparse_f16")
+           "fa2_last_error", "fa2_bwd_noalloc", "fa2_fwd_block_sparse_f16", "fa2_bwd_block_sparse_f16",
+           "fa2_fwd_olo", "fa2_bwd_olo", "fa2_bwd_stages_olo")
 DTYPES = (torch.bfloat16, torch.float16)
 
 BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL, BWD_DQ_ATOMIC = 1, 2, 4, 7, 8
@@ -61,6 +62,12 @@ def load(path: str | None = None):
     lib.fa2_bwd_stages.restype = i
     lib.fa2_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa2_bwd_noalloc.restype = i
+    lib.fa2_fwd_olo.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd_olo.restype = i
+    lib.fa2_bwd_olo.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_olo.restype = i
+    lib.fa2_bwd_stages_olo.argtypes = [ctypes.c_uint] + lib.fa2_bwd_olo.argtypes
+    lib.fa2_bwd_stages_olo.restype = i
     for name, like in (("fa2_fwd_f16", lib.fa2_fwd), ("fa2_bwd_f16", lib.fa2_bwd),
                        ("fa2_bwd_stages_f16", lib.fa2_bwd_stages)):
         fn = getattr(lib, name)
@@ -149,7 +156,14 @@ def _check_tensor(name: str, t, dtype, shape, device) -> None:
         raise ValueError(f"{name} must be on q's device {device}, got {t.device}")
 
 
-def check_forward_args(q, k, v, out=None, lse=None, require_gpu: bool = True):
+def _check_o_lo(q, o_lo) -> None:
+    if o_lo is not None:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("o_lo is for bfloat16 tensors")
+        _check_tensor("o_lo", o_lo, q.dtype, q.shape, q.device)
+
+
+def check_forward_args(q, k, v, out=None, lse=None, require_gpu: bool = True, o_lo=None):
     """The metadata checks of ``forward``: returns (B, Hq, Hkv, N, d).  Raises TypeError
     or ValueError before anything is allocated or launched."""
     B, Hq, Hkv, N, d = _dims(q, k, v, require_gpu)
@@ -157,14 +171,16 @@ def check_forward_args(q, k, v, out=None, lse=None, require_gpu: bool = True):
         _check_tensor("out", out, q.dtype, q.shape, q.device)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, (B, Hq, N), q.device)
+    _check_o_lo(q, o_lo)
     return B, Hq, Hkv, N, d
 
 
 def check_backward_args(q, k, v, o, lse, do, workspace=None, grads=None, nbytes: int = 0,
-                        require_gpu: bool = True):
+                        require_gpu: bool = True, o_lo=None):
     """The metadata checks of ``backward``: returns (B, Hq, Hkv, N, d)."""
     B, Hq, Hkv, N, d = _dims(q, k, v, require_gpu)
     _check_tensor("o", o, q.dtype, q.shape, q.device)
+    _check_o_lo(q, o_lo)
     _check_tensor("do", do, q.dtype, q.shape, q.device)
     _check_tensor("lse", lse, torch.float32, (B, Hq, N), q.device)
     if workspace is not None:
@@ -181,24 +197,29 @@ def check_backward_args(q, k, v, o, lse, do, workspace=None, grads=None, nbytes:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
-            lse: torch.Tensor | None = None):
+            lse: torch.Tensor | None = None, o_lo: torch.Tensor | None = None):
     """O = softmax(scale * q k^T [+ causal mask]) v and L (natural-log logsumexp per row).
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d] contiguous GPU tensors, all bf16 or all f16.
     Returns (o [B,Hq,N,d] in q's dtype, lse [B,Hq,N] fp32).  scale defaults to
-    1/sqrt(d).
+    1/sqrt(d).  ``o_lo`` (bf16 only): a tensor shaped like q that receives the
+    rounding residual of o (fa2_fwd_olo), for ``backward(..., o_lo=...)``.
     """
     lib = load()
-    B, Hq, Hkv, N, d = check_forward_args(q, k, v, out, lse)
+    B, Hq, Hkv, N, d = check_forward_args(q, k, v, out, lse, o_lo=o_lo)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    fwd = lib.fa2_fwd_f16 if q.dtype == torch.float16 else lib.fa2_fwd
-    st = fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
-             int(bool(causal)), float(scale), _stream_handle(q))
+    if o_lo is not None:
+        st = lib.fa2_fwd_olo(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(o_lo), _ptr(lse), B, Hq, Hkv,
+                             N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    else:
+        fwd = lib.fa2_fwd_f16 if q.dtype == torch.float16 else lib.fa2_fwd
+        st = fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                 int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return out, lse
 
@@ -211,7 +232,7 @@ def workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, stages: int = BWD
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, do: torch.Tensor, causal: bool = False,
              scale: float | None = None, workspace: torch.Tensor | None = None,
-             grads=None, stages: int = BWD_ALL):
+             grads=None, stages: int = BWD_ALL, o_lo: torch.Tensor | None = None):
     """dQ, dK, dV of sum(do * o) for the forward above (P rebuilt from lse).
 
     Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) in q's dtype.  A caller
@@ -219,21 +240,29 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     ``workspace_bytes(...)`` bytes (256-byte aligned), preallocated output
     tensors ``grads=(dq, dk, dv)``, and a subset of the launch ``stages``
     (issued in order; the workspace must carry over between partial calls).
+    ``o_lo`` (bf16 only): the forward's rounding residual of o; D is then formed
+    from o + o_lo (fa2_bwd_stages_olo).
     """
     lib = load()
     B, Hq, Hkv, N, d = _dims(q, k, v)
     nbytes = lib.fa2_bwd_stages_workspace_bytes(int(stages), B, Hq, Hkv, N, d)
-    check_backward_args(q, k, v, o, lse, do, workspace, grads, nbytes)
+    check_backward_args(q, k, v, o, lse, do, workspace, grads, nbytes, o_lo=o_lo)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
                                                   torch.empty_like(v))
-    bwd = lib.fa2_bwd_stages_f16 if q.dtype == torch.float16 else lib.fa2_bwd_stages
-    st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
+    if o_lo is not None:
+        st = lib.fa2_bwd_stages_olo(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse),
+                                    _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                    workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                    _stream_handle(q))
+    else:
+        bwd = lib.fa2_bwd_stages_f16 if q.dtype == torch.float16 else lib.fa2_bwd_stages
+        st = bwd(int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                 B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_handle(q))
     _check(st, lib)
     return dq, dk, dv
 

@@ -198,6 +198,39 @@ fa2_status fa2_bwd_stages_f16(unsigned stages, const void *Q, const void *K, con
                               void *stream);
 
 /*
+ * Split O: the forward's output carried to the backward at about 16
+ * significant bits instead of bf16's 8 (bf16 only, dense attention).
+ * The backward's D = rowsum(dO o O) (section 4 symbol table of the
+ * FlashAttention-2 summary page) is formed from the O it is given; from a
+ * bf16 O it inherits O's rounding, which moves dS = P o (dP - D) by
+ * P * dD on every key a row attends to and, summed over many rows, dK by
+ * more than the rounding of the products themselves.
+ *   fa2_fwd_olo: fa2_fwd that also writes O_lo [B,Hq,N,d] bf16, the
+ *     rounding residual of each output element, bf16(x - O) with x the fp32
+ *     value before its rounding to O (|O_lo| is at most half an ulp of O).
+ *     O and L are bitwise those of fa2_fwd.
+ *   fa2_bwd_olo / fa2_bwd_stages_olo: fa2_bwd / fa2_bwd_stages with
+ *     D = rowsum(dO o (O + O_lo)) (only FA2_BWD_PREPROCESS reads O_lo).
+ * O_lo must be a device buffer like O (16-byte aligned, [B,Hq,N,d] bf16),
+ * owned by the caller.  Errors: as fa2_fwd / fa2_bwd, plus
+ * FA2_ERR_INVALID_ARGUMENT when O_lo is NULL or misaligned, overlaps Q, K
+ * or V, in the forward overlaps O or L, or in the backward overlaps an
+ * output or the workspace.
+ */
+fa2_status fa2_fwd_olo(const void *Q, const void *K, const void *V, void *O, void *O_lo,
+                       float *L, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       void *stream);
+fa2_status fa2_bwd_olo(const void *Q, const void *K, const void *V, const void *O,
+                       const void *O_lo, const float *L, const void *dO, void *dQ, void *dK,
+                       void *dV, void *workspace, size_t workspace_bytes, int B, int Hq,
+                       int Hkv, int N, int d, int causal, float scale, void *stream);
+fa2_status fa2_bwd_stages_olo(unsigned stages, const void *Q, const void *K, const void *V,
+                              const void *O, const void *O_lo, const float *L, const void *dO,
+                              void *dQ, void *dK, void *dV, void *workspace,
+                              size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                              int causal, float scale, void *stream);
+
+/*
  * Block-sparse attention (FlashAttention paper page, aipaper.jasonlin.tech,
  * key contributions: the exact kernel restricted to a predefined block
  * sparsity pattern, skipping the blocks the pattern leaves out; limitations:

@@ -97,3 +97,22 @@ def test_entry_points_refuse_cpu_tensors_before_any_launch():
         fa2.backward(q, k, v, o, lse, do)
     with pytest.raises(ValueError, match="GPU"):
         fa2.forward_block_sparse(q, k, v, torch.ones(1, 1, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("bad", ["dtype", "shape", "noncontig", "device"])
+def test_o_lo_checked(bad):
+    """The split-O residual: a bf16 tensor shaped like q on q's device, for bf16 calls only."""
+    q, k, v = qkv()
+    o_lo = {"dtype": torch.empty(B, Hq, N, d, dtype=torch.float16),
+            "shape": torch.empty(B, Hq, N, d - 8, dtype=torch.bfloat16),
+            "noncontig": torch.empty(B, Hq, d, N, dtype=torch.bfloat16).transpose(2, 3),
+            "device": torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device="meta")}[bad]
+    with pytest.raises(ValueError, match="o_lo"):
+        fa2.check_forward_args(q, k, v, None, None, require_gpu=False, o_lo=o_lo)
+    o, do, lse = torch.empty_like(q), torch.empty_like(q), torch.empty(B, Hq, N)
+    with pytest.raises(ValueError, match="o_lo"):
+        fa2.check_backward_args(q, k, v, o, lse, do, require_gpu=False, o_lo=o_lo)
+    q16, k16, v16 = qkv(torch.float16)
+    with pytest.raises(TypeError, match="o_lo"):
+        fa2.check_forward_args(q16, k16, v16, require_gpu=False, o_lo=torch.empty_like(q16))
+    fa2.check_forward_args(q, k, v, require_gpu=False, o_lo=torch.empty_like(q))

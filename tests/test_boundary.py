@@ -271,3 +271,43 @@ def test_noalloc_backward_checks_before_any_hip_call(lib):
     assert noalloc(*p, 1, 1, 1, max_rows + 64, 64, 1, 0.125, None) == UNSUPPORTED
     assert b"scratch" in lib.fa2_last_error()
     assert noalloc(*p, 1, 33, 1, 65536, 64, 1, 0.125, None) == UNSUPPORTED
+
+
+def test_split_o_entry_points_check_before_any_hip_call(lib):
+    """fa2_fwd_olo / fa2_bwd_olo / fa2_bwd_stages_olo: the dense checks, then O_lo's own
+    (present, 16-byte aligned, overlapping no input; in the forward not O or L, in the
+    backward no output and not the workspace), all before any HIP call."""
+    q, k, v, o, L, olo = (addr(i) for i in range(6))
+    fwd = lib.fa2_fwd_olo
+    assert fwd(None, None, None, None, None, None, 0, 4, 2, 100, 128, 1, 0.1, None) == OK   # empty
+    assert fwd(q, k, v, o, None, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID
+    assert b"O_lo" in lib.fa2_last_error()
+    assert fwd(q, k, v, o, olo + 8, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID        # misaligned
+    assert fwd(q, k, v, o, q + 1024, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID       # inside Q
+    assert fwd(q, k, v, o, v, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID              # = V
+    assert fwd(q, k, v, o, o + 4096, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID       # inside O
+    assert fwd(q, k, v, o, L - 64, L, 2, 4, 2, 100, 128, 1, 0.1, None) == INVALID         # reaches into L
+    assert fwd(q, k, v, o, olo, L, 2, 6, 4, 100, 128, 1, 0.1, None) == INVALID            # Hq % Hkv first
+    assert fwd(q, k, v, o, olo, L, 2, 4, 2, 100, 96, 1, 0.1, None) == UNSUPPORTED
+    p = [addr(i) for i in range(10)]        # Q K V O L dO dQ dK dV ws
+    olo = addr(11)
+    nbytes = ws_bytes(lib)
+
+    def bwd(o_lo, ws=p[9], n=nbytes, d=128, Hq=4, stages=None):
+        args = (*p[:4], o_lo, *p[4:9], ws, n, 2, Hq, 2, 100, d, 1, 0.125, None)
+        if stages is None:
+            return lib.fa2_bwd_olo(*args)
+        return lib.fa2_bwd_stages_olo(stages, *args)
+
+    assert bwd(None) == INVALID
+    assert bwd(olo + 2) == INVALID                       # misaligned
+    assert bwd(p[0]) == INVALID                          # = Q
+    assert bwd(p[6] + 256) == INVALID                    # inside dQ
+    assert bwd(p[8]) == INVALID                          # = dV
+    assert bwd(p[9] + 256) == INVALID                    # inside the workspace
+    assert bwd(olo, n=nbytes - 1) == INVALID             # workspace too small
+    assert bwd(olo, d=96) == UNSUPPORTED
+    assert bwd(olo, Hq=6) == INVALID
+    for bad in (0, 16, 0xFFFFFFFF):
+        assert bwd(olo, stages=bad) == INVALID
+    assert bwd(olo, d=96, stages=1) == UNSUPPORTED
