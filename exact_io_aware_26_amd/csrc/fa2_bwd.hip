@@ -23,8 +23,8 @@
 //                    block mask: one mask row); dQ stays in registers over all
 //                    key blocks, recomputing S and dP, so no atomics are needed
 //                    and dQ is deterministic.
-//   bwd_kv256        d = 256: the K/V loop split over the head dim (two
-//                    workgroups per 128-key tile, 128 columns of dK, dV each).
+//   bwd_kv256f       d = 256: the K/V loop with 32-row query tiles (dK, dV of
+//                    the whole head dim in AGPRs).
 //   bwd_dq256        d = 256: the dQ pass with 32-key tiles.
 //   bwd_main         d = 256 in the atomic mode: the K/V loop with
 //                    register-staged tiles and atomically added dQ.
@@ -1752,34 +1752,46 @@ void bwd_kv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// bwd_kv256: the K/V-tile loop for d = 256 (dQ in its own pass), the d = 128
-// design split over the head dim: a pair of workgroups shares each 128-key
-// tile, both computing s = Q K^T and dp = dO V^T over all 256 dims (K and V of
-// the wave's keys as register operands), each accumulating dK and dV for 128
-// of the columns.  That costs the s and dp products twice, but the whole K/V
-// rows and 128 columns of both accumulators (held in AGPRs) fit one wave's
-// registers.  64-row query tiles (Q, dO: 32 KiB each) are copied two deep.
+// bwd_kv256f: the K/V-tile loop for d = 256 with the whole head dim of dK and
+// dV in one workgroup, so s = Q K^T and dp = dO V^T are computed once per key
+// tile.  Each wave owns 32 keys: their K and V rows (all 256 dims, 128 VGPRs)
+// are the B operands of s and dp, and their dK and dV (32 keys x 256 dims
+// each, all 256 AGPRs) accumulate from matrix products issued as inline
+// assembly.  That leaves room for one 32-row query block of scores at a time,
+// so query tiles have 32 rows, copied into a ring of four LDS buffers two
+// tiles ahead.  A tile is a fixed program of 64 products:
+//   s, dp of this tile's block         (A: Q / dO rows, B: K / V of this lane)
+//   dV, dK over the previous block     | P, dS of this block, element by element
+// (A: dO^T / Q^T read transposed from the previous tile's buffer, B: that
+// block's P and dS, packed in registers), so the vector work of a block runs
+// beside the products of the block before it; a last program without s, dp
+// adds the final block.  Block-sparse (SPARSE): the key tile is one mask
+// column, and the walk is the list of 32-row tiles of the query blocks its
+// mask column keeps (causal: at or below the diagonal).
 template <bool CAUSAL, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void bwd_kv256_kernel(const BwdParams p) {
-    constexpr int D = 256, DH = 128;          // head dim; dK / dV columns per workgroup
-    constexpr int NW = 4, BC = 32 * NW, BR = kBwdRowPad;
+void bwd_kv256f_kernel(const BwdParams p) {
+    constexpr int D = 256;
+    constexpr int NW = 4, BC = 32 * NW, BR = 32;
     constexpr int RB = 2 * D;                 // bytes per row of the Q / dO tiles
     constexpr int kTile = BR * RB;
     constexpr int KSD = D / 16;               // reduction steps over the head dim
-    constexpr int NBD = DH / 32;              // 32-wide blocks of this workgroup's dK / dV columns
+    constexpr int NBD = D / 32;               // 32-wide head-dim blocks of dK / dV
     constexpr int RPI = 1024 / RB;            // tile rows per wave copy instruction
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int PERW = kTile / 1024 / NW;   // copy instructions per wave per tensor
-    static_assert(BR == 64 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
-    // Two LDS arrays of one query tile each, [Q | dO | L log2 e | -D], 512-byte
-    // aligned: every read of a tile is a per-tile lane base (with the array's
-    // address folded in) XOR a constant, plus an immediate offset below 64 KiB.
-    constexpr int kBuf = 2 * kTile + 2 * BR * 4;
-    static_assert(kBuf % 512 == 0, "tile arrays keep the 512-byte alignment the column XOR needs");
-    __shared__ __attribute__((aligned(512))) char Ta0[kBuf], Ta1[kBuf];
+    static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    // L log2 e and -D travel as the kBwdRowPad-row chunk holding the tile (the
+    // workspace rows are padded to whole chunks, so the copy stays in bounds).
+    constexpr int LR = kBwdRowPad;
+    static_assert(LR % BR == 0 && LR == 64, "one copy instruction per L / D chunk");
+    constexpr int kBuf = 2 * kTile + 2 * LR * 4;
+    static_assert(kBuf % 512 == 0, "tile arrays keep the 512-byte alignment the swizzle needs");
+    __shared__ __attribute__((aligned(512))) char Ta0[kBuf], Ta1[kBuf], Ta2[kBuf], Ta3[kBuf];
     FA2_LDS char* const T0 = (FA2_LDS char*)Ta0;
     FA2_LDS char* const T1 = (FA2_LDS char*)Ta1;
+    FA2_LDS char* const T2 = (FA2_LDS char*)Ta2;
+    FA2_LDS char* const T3 = (FA2_LDS char*)Ta3;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1787,13 +1799,11 @@ void bwd_kv256_kernel(const BwdParams p) {
     const int g = lane >> 5;
     const int li = lane & 31;
 
-    // Workgroup pairs (ids 2i, 2i + 1) share a key tile: columns [0, 128) and
-    // [128, 256) of its dK and dV.
-    const int half = blockIdx.x & 1;
-    const int wg = blockIdx.x >> 1;
+    // Workgroups in order of decreasing work (causal: the first key tiles have
+    // the most query tiles).
     const int BHk = p.B * p.Hkv;
-    const int kvtile = wg / BHk;
-    const int bh = wg - kvtile * BHk;
+    const int kvtile = blockIdx.x / BHk;
+    const int bh = blockIdx.x - kvtile * BHk;
     const int b = bh / p.Hkv;
     const int hk = bh - b * p.Hkv;
     const int N = p.N;
@@ -1803,15 +1813,15 @@ void bwd_kv256_kernel(const BwdParams p) {
     const size_t khead = ((size_t)b * p.Hkv + hk) * (size_t)N * D;
 
     el8 kf[KSD], vf[KSD];
+    {
+        // Rows past N repeat row N - 1: a lane's key only meets its own dK, dV
+        // column, which is not stored.
+        const size_t krow = khead + (size_t)min(kv, N - 1) * D;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-        if (kv < N) {
-            kx = global_load16(p.K + khead + (size_t)kv * D + 16 * ks + 8 * g);
-            vx = global_load16(p.V + khead + (size_t)kv * D + 16 * ks + 8 * g);
+        for (int ks = 0; ks < KSD; ++ks) {
+            kf[ks] = as_el8(global_load16(p.K + krow + 16 * ks + 8 * g));
+            vf[ks] = as_el8(global_load16(p.V + krow + 16 * ks + 8 * g));
         }
-        kf[ks] = as_el8(kx);
-        vf[ks] = as_el8(vx);
     }
     f32x16 dv[NBD], dk[NBD];
 #pragma unroll
@@ -1821,10 +1831,7 @@ void bwd_kv256_kernel(const BwdParams p) {
     }
 
     // Query tiles: for each of the G query heads sharing this K/V head, the
-    // 64-row tiles from the first one the causal mask lets through.  Block-
-    // sparse: the key tile is one mask column; the tiles of the query blocks
-    // whose mask byte in it is set (causal: at or below the diagonal), from an
-    // LDS list built by wave 0 (each of the pair's workgroups builds its own).
+    // 32-row tiles from the first one the causal mask lets through.
     const int n_qt = (N + BR - 1) / BR;
     const int i_begin = CAUSAL ? kv0 / BR : 0;
     int n_i;
@@ -1847,16 +1854,14 @@ void bwd_kv256_kernel(const BwdParams p) {
         n_i = n_qt - i_begin;
     }
     const int n_iter = n_i * p.G;
-    // First row of query tile i of the walk.
     auto qrow_at = [&](int i) -> int {
         if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl[i]) * BR;
         else return (i_begin + i) * BR;
     };
 
-    // Copy of query tile `it` into LDS as NCOPY wave instructions, which the
-    // tile program spreads over its first slots: Q and dO rows
-    // (clamped to N-1 past the end; those rows have L = +inf, so P = dS = 0),
-    // and the padded L log2 e and -D rows (waves 0 and 2 both copy L, 1 and 3
+    // Copy of query tile `it` into LDS as NCOPY wave instructions: Q and dO
+    // rows (clamped to N-1 past the end; those rows have L = +inf, so P = dS =
+    // 0), and the L log2 e and -D chunk (waves 0 and 2 both copy L, 1 and 3
     // both copy -D: identical bytes, so every wave issues the same number of
     // copies).
     constexpr int NCOPY = 2 * PERW + 1;
@@ -1871,7 +1876,7 @@ void bwd_kv256_kernel(const BwdParams p) {
         const int hq = hk * p.G + it / n_i;
         const int qt0 = qrow_at(it % n_i);
         const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)N + qt0;
-        const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + qt0;
+        const size_t prow = ((size_t)b * p.Hq + hq) * (size_t)p.Npad + (qt0 & ~(LR - 1));
         TileCopy c;
         c.qbase = reinterpret_cast<const char*>(p.Q + qrow0 * D);
         c.obase = reinterpret_cast<const char*>(p.dO + qrow0 * D);
@@ -1891,7 +1896,7 @@ void bwd_kv256_kernel(const BwdParams p) {
             if (j < PERW) copy_to_lds16(c.qbase, off, c.T + (wave * PERW + i) * 1024);
             else copy_to_lds16(c.obase, off, c.T + kTile + (wave * PERW + i) * 1024);
         } else {
-            copy_to_lds4(c.ld_src, 4 * lane, c.T + 2 * kTile + (wave & 1) * BR * 4);
+            copy_to_lds4(c.ld_src, 4 * lane, c.T + 2 * kTile + (wave & 1) * LR * 4);
         }
     };
     auto copy_tile = [&](int it, FA2_LDS char* T) {
@@ -1900,155 +1905,124 @@ void bwd_kv256_kernel(const BwdParams p) {
         for (int j = 0; j < NCOPY; ++j) copy_part(c, j);
     };
 
-    // LDS operand addresses: the swizzle only flips bits 4.. of a row's byte
-    // offset below RB, so they are a per-lane base XOR a constant (32*ks for
-    // Q / dO rows, chunk 2*ks + g; 64*db for the transposed reads).
+    // LDS operand addresses: per-lane bases XOR a constant (32*ks for Q / dO
+    // rows, chunk 2*ks + g; 64*db for the transposed reads).
     const int j16 = lane & 15;
     const int xq = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
     const int r1 = 4 * g + (j16 >> 2), r2 = r1 + 8;
     const int kb_lane = li * RB + 16 * (g ^ swz<RB>(li));
-    // Transposed reads address this workgroup's half of the columns (bit 8 of a
-    // 512-byte row).
-    const int vb1_lane = (r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1))) ^ (256 * half);
-    const int vb2_lane = (r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2))) ^ (256 * half);
+    const int vb1_lane = r1 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r1));
+    const int vb2_lane = r2 * RB + 8 * (j16 & 1) + 16 * (xq ^ swz<RB>(r2));
 
-    // One query tile as a fixed program of matrix products, one per slot
-    // (NS = 2 * D/16 products of s and dp per 32-row block, NG = 4 * D/32 of
-    // dV and dK; 16, 16 for d = 128):
-    //   s, dp of block 0          (A: Q / dO rows, B: K / V of this lane)
-    //   s, dp of block 1          | P, dS of block 0, 16 / NS elements per slot
-    //   dV, dK over block 0       | P, dS of block 1, 16 / NG elements per slot
-    //   dV, dK over block 1
-    // Each product's A operand is read from LDS kPrefetch slots ahead; a
-    // scheduling fence between slots keeps this order, so the compiler waits
-    // only for the read a product needs.
-    constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = 2 * NS + 2 * NG;
-    constexpr int kPrefetch = 3;                    // 4 would spill here (512 registers)
-    static_assert(NS >= 16 && NG >= 16, "slot program shape");
-    static_assert(NCOPY <= NP, "the copies of the next tile fit in one tile program");
-    auto tile = [&](const FA2_LDS char* T, int qt0, const TileCopy& cp) {
-        // Lane bases with the tile's address folded in, rebuilt per tile (opaque
-        // to the compiler) rather than held across the loop.
-        const uint32_t tb = (uint32_t)(uintptr_t)T;
-        uint32_t kb = tb + kb_lane, vb1 = tb + vb1_lane, vb2 = tb + vb2_lane, lb = tb + 2 * kTile + 16 * g;
+    constexpr int NS = 2 * KSD;               // s, dp products of a block
+    constexpr int NG = 4 * NBD;               // dV, dK products of a block
+    constexpr int NP = NS + NG;
+    constexpr int kPrefetch = 4;
+    static_assert(NCOPY < NS, "the copies of a tile fit in the first phase");
+    uint32_t qp[8], qd[8];                    // P, dS of the previous block, packed
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        qp[r] = 0u;
+        qd[r] = 0u;
+    }
+    // Tile program; with DRAIN only the dV, dK products of the previous block.
+    auto tile = [&](auto drain_tag, const FA2_LDS char* T, const FA2_LDS char* Tp, int qt0,
+                    const TileCopy& cp) __attribute__((always_inline)) {
+        constexpr bool DRAIN = decltype(drain_tag)::value;
+        const uint32_t tb = (uint32_t)(uintptr_t)T, tp = (uint32_t)(uintptr_t)Tp;
+        uint32_t kb = tb + kb_lane, vb1 = tp + vb1_lane, vb2 = tp + vb2_lane;
+        uint32_t lb = tb + 2 * kTile + 16 * g + 4 * (qt0 & (LR - 1));
         asm volatile("" : "+v"(kb), "+v"(vb1), "+v"(vb2), "+v"(lb));
         auto at = [](uint32_t a) { return (const FA2_LDS char*)(uintptr_t)a; };
         // Four consecutive floats of the L log2 e (which = 0) or -D (which = 1)
-        // rows: queries 32 * blk + 8 * rl + 4g .. +3, the order of a score
+        // rows of this block: queries 8 * rl + 4g .. +3, the order of a score
         // accumulator's registers 4 rl .. 4 rl + 3.
-        auto ld_rows = [&](int which, int blk, int rl) {
-            return *reinterpret_cast<const FA2_LDS f32x4*>(at(lb) + 4 * (which * BR + 32 * blk + 8 * rl));
+        auto ld_rows = [&](int which, int rl) {
+            return *reinterpret_cast<const FA2_LDS f32x4*>(at(lb) + 4 * (which * LR + 8 * rl));
         };
-        f32x16 sc[2], dpc[2];
-        uint32_t pp[2][8], pd[2][8];
-        f32x4 lv[2][4];
-        f32x16 nd[2];                        // -D of each block: where its dP products start
-        auto load_nd = [&](int blk, int rl) {
-            const f32x4 v = ld_rows(1, blk, rl);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
-        };
-        // A operand of product k.
+        f32x16 sc, dpc, nd;
+        f32x4 lv[4];
+        uint32_t pp[8], pd[8];
         auto load_a = [&](int k) -> el8 {
-            if (k < 2 * NS) {
-                const int blk = k / NS, ks = (k % NS) >> 1;
-                const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
-                return as_el8(lds_load16(at(kb ^ (32 * ks)) + off));
+            if (k < NS) {
+                const int ks = k >> 1;
+                return as_el8(lds_load16(at(kb ^ (32 * ks)) + ((k & 1) ? kTile : 0)));   // dO or Q rows
             }
-            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
-            const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
+            const int j = k - NS, h = j >> 4, db = (j & 15) >> 1;
+            const int off = ((j & 1) ? 0 : kTile) + 16 * h * RB;                      // Q or dO, transposed
             return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
         };
         auto product = [&](int k, el8 a) {
-            if (k < 2 * NS) {
-                const int blk = k / NS, ks = (k % NS) >> 1;
-                if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
-                else sc[blk] = mfma32(a, kf[ks], ks == 0 ? zero16() : sc[blk]);
+            if (k < NS) {
+                const int ks = k >> 1;
+                if (k & 1) dpc = mfma32(a, vf[ks], ks == 0 ? nd : dpc);                 // dp - D
+                else sc = mfma32(a, kf[ks], ks == 0 ? zero16() : sc);
                 return;
             }
-            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
-            // Issued as assembly to keep the accumulators in AGPRs (with the
-            // whole head dim of K and V as operands they do not fit in VGPRs).
-            if (jj & 1) {
-                const el8 bs = as_el8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
+            const int j = k - NS, h = j >> 4, db = (j & 15) >> 1;
+            // Issued as assembly to keep the accumulators in AGPRs.
+            if (j & 1) {
+                const el8 bs = as_el8(u32x4{qd[4 * h], qd[4 * h + 1], qd[4 * h + 2], qd[4 * h + 3]});
                 f32x16 c = dk[db];
                 asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bs));
                 dk[db] = c;
             } else {
-                const el8 bp = as_el8(u32x4{pp[blk][4 * h], pp[blk][4 * h + 1], pp[blk][4 * h + 2], pp[blk][4 * h + 3]});
+                const el8 bp = as_el8(u32x4{qp[4 * h], qp[4 * h + 1], qp[4 * h + 2], qp[4 * h + 3]});
                 f32x16 c = dv[db];
                 asm volatile(FA2_MFMA_32X32X16 " %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(bp));
                 dv[db] = c;
             }
         };
-        // Element r of P and dS of block blk (query 8*(r/4) + 4g + r%4 of the
-        // block, this lane's key) in three stages -- c*s - L log2 e, exp2, then
-        // dS and the bf16 packing -- run for elements r, r-1, r-2 in one slot,
-        // so the instructions of a slot do not wait on each other.
-        // Each stage's result is pinned in its slot (an empty asm that redefines
-        // it), or the compiler sinks the arithmetic down to the dV / dK products
-        // that consume it and the slots before those get no vector work.
+        // Element r of P and dS (query 8*(r/4) + 4g + r%4 of the block, this
+        // lane's key) in three stages -- c*s - L log2 e, exp2, then dS and the
+        // bf16 packing -- each pinned in its slot.
         auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
         auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
-        auto stage_a = [&](int blk, int r) {
-            float x = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]);
+        auto stage_a = [&](int r) {
+            float x = fmaf(sc[r], p.c, -lv[r >> 2][r & 3]);
             pin(x);
-            sc[blk][r] = x;
+            sc[r] = x;
         };
-        auto stage_b = [&](int blk, int r) {
-            float x = exp2_fast(sc[blk][r]);
+        auto stage_b = [&](int r) {
+            float x = exp2_fast(sc[r]);
             pin(x);
-            sc[blk][r] = x;
+            sc[r] = x;
         };
-        auto stage_c = [&](int blk, int r) {
-            const float pr = sc[blk][r];
-            float ds = pr * dpc[blk][r];
+        auto stage_c = [&](int r) {
+            const float pr = sc[r];
+            float ds = pr * dpc[r];
             pin(ds);
-            dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
+            dpc[r] = ds;
             if (r & 1) {
-                uint32_t a = pack_el(sc[blk][r - 1], pr), c = pack_el(dpc[blk][r - 1], ds);
+                uint32_t a = pack_el(sc[r - 1], pr), c = pack_el(dpc[r - 1], ds);
                 pin_u(a);
                 pin_u(c);
-                pp[blk][r >> 1] = a;
-                pd[blk][r >> 1] = c;
+                pp[r >> 1] = a;
+                pd[r >> 1] = c;
             }
         };
-        // Vector work of slot k: L of a block is read half a block of products
-        // before its P, -D of block 1 with L of block 0; then the staged elements.
         auto vector_work = [&](int k) {
-            const int rl = k - NS / 2;                        // slots NS/2 .. NS/2+3
-            if (rl >= 0 && rl < 4) {
-                lv[0][rl] = ld_rows(0, 0, rl);
-                load_nd(1, rl);
-            }
-            const int rl1 = k - (NS + NS / 2);                // block 1's L
-            if (rl1 >= 0 && rl1 < 4) lv[1][rl1] = ld_rows(0, 1, rl1);
+            if constexpr (!DRAIN) {
+                const int rl = k - NS / 2;                    // L of the block, half a phase ahead
+                if (rl >= 0 && rl < 4) lv[rl] = ld_rows(0, rl);
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int start = blk ? 2 * NS : NS;          // first slot of the block's elements
-                const int S = blk ? NG : NS;                  // slots of the phase they run in
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {                // element r starts at slot r * S / 16
-                    const int t = k - start - r * S / 16;
-                    if (t == 2) stage_c(blk, r);
-                    if (t == 1) stage_b(blk, r);
-                    if (t == 0) stage_a(blk, r);
+                for (int r = 0; r < 16; ++r) {                // element r starts at slot NS + r * (NG - 3) / 15
+                    const int t = k - NS - r * (NG - 3) / 15;
+                    if (t == 2) stage_c(r);
+                    if (t == 1) stage_b(r);
+                    if (t == 0) stage_a(r);
                 }
             }
         };
-        // Causal mask of block blk, once its scores are complete: only a block
-        // that starts below this wave's last key has keys above the diagonal
-        // (one or two blocks per query head in a wave's whole loop).
-        auto mask = [&](int blk) {
-            if (CAUSAL && qt0 + 32 * blk < kw0 + 31) {
+        if constexpr (!DRAIN) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk][i] = -kInf;
+            for (int rl = 0; rl < 4; ++rl) {                  // -D: where the dP products start
+                const f32x4 v = ld_rows(1, rl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nd[4 * rl + e] = v[e];
             }
-        };
-        // -D of block 0 before the first operands: its dP products start at slot 1.
-#pragma unroll
-        for (int rl = 0; rl < 4; ++rl) load_nd(0, rl);
+        }
+        constexpr int K0 = DRAIN ? NS : 0;
         el8 abuf[kPrefetch];
         auto slot = [&](int k) {
             __builtin_amdgcn_sched_barrier(0);
@@ -2056,37 +2030,66 @@ void bwd_kv256_kernel(const BwdParams p) {
             if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
             product(k, a);
             vector_work(k);
-            if (k < NCOPY) copy_part(cp, k);                // the next tile's copies: first slots
+            if (!DRAIN && k >= 1 && k <= NCOPY) copy_part(cp, k - 1);
         };
 #pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
+        for (int k = K0; k < K0 + kPrefetch; ++k) abuf[k % kPrefetch] = load_a(k);
+        if constexpr (!DRAIN) {
 #pragma unroll
-        for (int k = 0; k < NS; ++k) slot(k);
-        mask(0);
+            for (int k = 0; k < NS; ++k) slot(k);
+            // Causal mask, once the scores are complete: only a block that starts
+            // below this wave's last key has keys above the diagonal.
+            if (CAUSAL && qt0 < kw0 + 31) {
 #pragma unroll
-        for (int k = NS; k < 2 * NS; ++k) slot(k);
-        mask(1);
+                for (int i = 0; i < 16; ++i)
+                    if (kv > qt0 + 8 * (i >> 2) + 4 * g + (i & 3)) sc[i] = -kInf;
+            }
+        }
 #pragma unroll
-        for (int k = 2 * NS; k < NP; ++k) slot(k);
+        for (int k = NS; k < NP; ++k) slot(k);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!DRAIN) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                qp[r] = pp[r];
+                qd[r] = pd[r];
+            }
+        }
     };
 
-    auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
-        // The other buffer was released by the barrier ending the previous
-        // step.  Copies past the last tile repeat it into it (never read).
-        tile(T, qrow_at(it % n_i), plan_copy(min(it + 1, n_iter - 1), Tw));
-        wait_vm_all();                  // tile it+1 has landed
+    // Step it reads tile it (and the previous tile's buffer) and copies tile
+    // it + 2 into the buffer released by the barrier ending step it - 1;
+    // copies past the last tile repeat it into a buffer never read, so every
+    // step issues and waits for the same count.
+    auto step = [&](int it, const FA2_LDS char* T, const FA2_LDS char* Tp, FA2_LDS char* Tw)
+        __attribute__((always_inline)) {
+        tile(std::false_type{}, T, Tp, qrow_at(it % n_i), plan_copy(min(it + 2, n_iter - 1), Tw));
+        wait_vm_keep<NCOPY>();          // tile it+1, issued one step earlier, has landed
         barrier_lds();
     };
 
     if (n_iter > 0) {
+        // Tile -1 (the previous buffer of tile 0): zero Q and dO, so the first
+        // dV, dK products add nothing.
+        for (int i = tid; i < 2 * kTile / 16; i += 64 * NW) lds_store16(T3 + 16 * i, u32x4{0, 0, 0, 0});
         copy_tile(0, T0);
+        copy_tile(min(1, n_iter - 1), T1);
         wait_vm_all();
         __syncthreads();
-        for (int it = 0; it < n_iter; it += 2) {
-            step(it, T0, T1);
-            if (it + 1 < n_iter) step(it + 1, T1, T0);
+        for (int it = 0; it < n_iter; it += 4) {
+            step(it, T0, T3, T2);
+            if (it + 1 < n_iter) {
+                step(it + 1, T1, T0, T3);
+                if (it + 2 < n_iter) {
+                    step(it + 2, T2, T1, T0);
+                    if (it + 3 < n_iter) step(it + 3, T3, T2, T1);
+                }
+            }
         }
+        // The last block's dV, dK, from the last tile's buffer.
+        const int t = (n_iter - 1) & 3;
+        const FA2_LDS char* Tl = t == 0 ? T0 : t == 1 ? T1 : t == 2 ? T2 : T3;
+        tile(std::true_type{}, Tl, Tl, 0, plan_copy(0, T0));
         wait_vm_all();
     }
     // The accumulators were last written by matrix products issued from inline
@@ -2101,7 +2104,7 @@ void bwd_kv256_kernel(const BwdParams p) {
         for (int db = 0; db < NBD; ++db)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const int d0 = DH * half + 32 * db + 8 * rq + 4 * g;
+                const int d0 = 32 * db + 8 * rq + 4 * g;
                 *reinterpret_cast<u32x2*>(dVr + d0) =
                     u32x2{pack_el(dv[db][4 * rq], dv[db][4 * rq + 1]),
                           pack_el(dv[db][4 * rq + 2], dv[db][4 * rq + 3])};
@@ -2180,9 +2183,9 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
             grid = (long)p.B * p.Hkv * ((p.N + BC - 1) / BC);
             threads = 64 * BwdCfg<D>::NW;
         } else {
-            fn = p.bmask ? reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL, true>)
-                         : reinterpret_cast<const void*>(&bwd_kv256_kernel<CAUSAL, false>);
-            grid = 2L * p.B * p.Hkv * ((p.N + 127) / 128);       // two column halves per key tile
+            fn = p.bmask ? reinterpret_cast<const void*>(&bwd_kv256f_kernel<CAUSAL, true>)
+                         : reinterpret_cast<const void*>(&bwd_kv256f_kernel<CAUSAL, false>);
+            grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
             threads = 256;
         }
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
