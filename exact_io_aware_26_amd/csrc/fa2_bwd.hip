@@ -1394,11 +1394,17 @@ void bwd_dq256_kernel(const BwdParams p) {
 //                                  B: P / dS straight from the s / dp registers,
 // since a score accumulator register holds the 8 queries, in the order of the
 // transposed reads, that the B operand of a 16-query step needs.  Within a
-// tile, the vector work of one query block overlaps the products of the other.
-template <int D, bool CAUSAL, bool SPARSE>
+// tile, the vector work of one query block overlaps the products of the next.
+// NB query blocks per tile: 2 (64-row tiles), or 4 at d = 64 when N is a
+// multiple of 128 (128-row tiles, so a tile's fixed costs -- barrier, waits,
+// copies, the operand pipeline's restart -- spread over as many products as
+// at d = 128; the workspace rows are padded to 64 only, so the 128-row tiles
+// must not pass N).
+template <int D, bool CAUSAL, bool SPARSE, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_kv_kernel(const BwdParams p) {
-    constexpr int NW = 4, BC = 32 * NW, BR = kBwdRowPad;
+    static_assert(NB == 2 || (NB == 4 && D == 64 && !SPARSE), "tile shapes");
+    constexpr int NW = 4, BC = 32 * NW, BR = 32 * NB;
     constexpr int RB = 2 * D;                 // bytes per row of the Q / dO tiles
     constexpr int kTile = BR * RB;
     constexpr int KSD = D / 16;               // reduction steps over the head dim
@@ -1406,7 +1412,7 @@ void bwd_kv_kernel(const BwdParams p) {
     constexpr int RPI = 1024 / RB;            // tile rows per wave copy instruction
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int PERW = kTile / 1024 / NW;   // copy instructions per wave per tensor
-    static_assert(BR == 64 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
+    static_assert(BR % kBwdRowPad == 0 && PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
     // One LDS array per buffered query tile, [Q | dO | L log2 e | -D], each
     // 256-byte aligned: every read of a tile is a per-tile lane base (with the
     // array's address folded in) XOR a constant, plus an immediate offset
@@ -1534,7 +1540,10 @@ void bwd_kv_kernel(const BwdParams p) {
             if (j < PERW) copy_to_lds16(c.qbase, off, c.T + (wave * PERW + i) * 1024);
             else copy_to_lds16(c.obase, off, c.T + kTile + (wave * PERW + i) * 1024);
         } else {
-            copy_to_lds4(c.ld_src, 4 * lane, c.T + 2 * kTile + (wave & 1) * BR * 4);
+            // 64 rows per instruction: with 128-row tiles waves 0, 2 copy the
+            // two halves of L, waves 1, 3 those of -D.
+            const int lh = BR == 128 ? wave >> 1 : 0;
+            copy_to_lds4(c.ld_src + 64 * lh, 4 * lane, c.T + 2 * kTile + (wave & 1) * BR * 4 + 256 * lh);
         }
     };
     auto copy_tile = [&](int it, FA2_LDS char* T) {
@@ -1558,15 +1567,23 @@ void bwd_kv_kernel(const BwdParams p) {
     // dV and dK; 16, 16 for d = 128):
     //   s, dp of block 0          (A: Q / dO rows, B: K / V of this lane)
     //   s, dp of block 1          | P, dS of block 0, 16 / NS elements per slot
-    //   dV, dK over block 0       | P, dS of block 1, 16 / NG elements per slot
-    //   dV, dK over block 1
+    //   ...
+    //   s, dp of block NB-1       | P, dS of block NB-2
+    //   dV, dK over block 0       | P, dS of block NB-1, 16 / NG elements per slot
+    //   dV, dK over blocks 1 .. NB-1
     // Each product's A operand is read from LDS kPrefetch slots ahead; a
     // scheduling fence between slots keeps this order, so the compiler waits
-    // only for the read a product needs.
-    constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = 2 * NS + 2 * NG;
+    // only for the read a product needs.  A block's scores live from its s, dp
+    // products to the end of its P, dS (two slots into block b+2's products),
+    // hence three score buffers.
+    constexpr int NS = 2 * KSD, NG = 4 * NBD, NP = NB * NS + NB * NG;
     constexpr int kPrefetch = 4;
     static_assert(16 % NS == 0 && 16 % NG == 0 && NS >= 8, "slot program shape");
-    static_assert(NCOPY <= NG, "the copies of the next tile fit in the last phase");
+    static_assert(NCOPY <= NB * NG, "the copies of the next tile fit in the dV, dK phases");
+    // The next tile's copies take the last slots of the last dV, dK phase (and
+    // of the one before it when they do not fit).
+    constexpr int kCopy0 = NB * NS + (NB - 1) * NG - (NCOPY > NG ? NCOPY - NG : 0);
+    constexpr int NSB = NB > 2 ? 3 : 2;       // score buffers
     auto tile = [&](const FA2_LDS char* T, int qt0, const TileCopy& cp) {
         // Lane bases with the tile's address folded in, rebuilt per tile (opaque
         // to the compiler) rather than held across the loop.
@@ -1580,34 +1597,34 @@ void bwd_kv_kernel(const BwdParams p) {
         auto ld_rows = [&](int which, int blk, int rl) {
             return *reinterpret_cast<const FA2_LDS f32x4*>(at(lb) + 4 * (which * BR + 32 * blk + 8 * rl));
         };
-        f32x16 sc[2], dpc[2];
-        uint32_t pp[2][8], pd[2][8];
-        f32x4 lv[2][4];
-        f32x16 nd[2];                        // -D of each block: where its dP products start
+        f32x16 sc[NSB], dpc[NSB];            // block b's scores in buffer b % NSB
+        uint32_t pp[NB][8], pd[NB][8];
+        f32x4 lv[2][4];                      // block b's L in buffer b % 2
+        f32x16 nd[2];                        // -D of block b (buffer b % 2): where its dP products start
         auto load_nd = [&](int blk, int rl) {
             const f32x4 v = ld_rows(1, blk, rl);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) nd[blk][4 * rl + e] = v[e];
+            for (int e = 0; e < 4; ++e) nd[blk % 2][4 * rl + e] = v[e];
         };
         // A operand of product k.
         auto load_a = [&](int k) -> el8 {
-            if (k < 2 * NS) {
+            if (k < NB * NS) {
                 const int blk = k / NS, ks = (k % NS) >> 1;
                 const int off = ((k & 1) ? kTile : 0) + 32 * blk * RB;          // dO or Q rows
                 return as_el8(lds_load16(at(kb ^ (32 * ks)) + off));
             }
-            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            const int j = k - NB * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
             const int off = ((jj & 1) ? 0 : kTile) + 16 * (2 * blk + h) * RB;   // Q or dO, transposed
             return cat_tr(lds_load_tr(at(vb1 ^ (64 * db)) + off), lds_load_tr(at(vb2 ^ (64 * db)) + off));
         };
         auto product = [&](int k, el8 a) {
-            if (k < 2 * NS) {
-                const int blk = k / NS, ks = (k % NS) >> 1;
-                if (k & 1) dpc[blk] = mfma32(a, vf[ks], ks == 0 ? nd[blk] : dpc[blk]);   // dp - D
-                else sc[blk] = mfma32(a, kf[ks], ks == 0 ? zero16() : sc[blk]);
+            if (k < NB * NS) {
+                const int blk = k / NS, ks = (k % NS) >> 1, sb = blk % NSB;
+                if (k & 1) dpc[sb] = mfma32(a, vf[ks], ks == 0 ? nd[blk % 2] : dpc[sb]);   // dp - D
+                else sc[sb] = mfma32(a, kf[ks], ks == 0 ? zero16() : sc[sb]);
                 return;
             }
-            const int j = k - 2 * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
+            const int j = k - NB * NS, blk = j / NG, jj = j % NG, h = jj / (NG / 2), db = (jj % (NG / 2)) >> 1;
             if (jj & 1) {
                 const el8 bs = as_el8(u32x4{pd[blk][4 * h], pd[blk][4 * h + 1], pd[blk][4 * h + 2], pd[blk][4 * h + 3]});
                 dk[db] = mfma32(a, bs, dk[db]);
@@ -1626,42 +1643,46 @@ void bwd_kv_kernel(const BwdParams p) {
         auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
         auto pin_u = [](uint32_t& x) { asm volatile("" : "+v"(x)); };
         auto stage_a = [&](int blk, int r) {
-            float x = fmaf(sc[blk][r], p.c, -lv[blk][r >> 2][r & 3]);
+            float x = fmaf(sc[blk % NSB][r], p.c, -lv[blk % 2][r >> 2][r & 3]);
             pin(x);
-            sc[blk][r] = x;
+            sc[blk % NSB][r] = x;
         };
         auto stage_b = [&](int blk, int r) {
-            float x = exp2_fast(sc[blk][r]);
+            float x = exp2_fast(sc[blk % NSB][r]);
             pin(x);
-            sc[blk][r] = x;
+            sc[blk % NSB][r] = x;
         };
         auto stage_c = [&](int blk, int r) {
-            const float pr = sc[blk][r];
-            float ds = pr * dpc[blk][r];
+            const int sb = blk % NSB;
+            const float pr = sc[sb][r];
+            float ds = pr * dpc[sb][r];
             pin(ds);
-            dpc[blk][r] = ds;                // the fp32 values are kept until their pair is packed
+            dpc[sb][r] = ds;                 // the fp32 values are kept until their pair is packed
             if (r & 1) {
-                uint32_t a = pack_el(sc[blk][r - 1], pr), c = pack_el(dpc[blk][r - 1], ds);
+                uint32_t a = pack_el(sc[sb][r - 1], pr), c = pack_el(dpc[sb][r - 1], ds);
                 pin_u(a);
                 pin_u(c);
                 pp[blk][r >> 1] = a;
                 pd[blk][r >> 1] = c;
             }
         };
-        // Vector work of slot k: L of a block is read half a block of products
-        // before its P, -D of block 1 with L of block 0; then the staged elements.
+        // Vector work of slot k: L of block b is read in slots b*NS + NS/2 ..
+        // +3, half a block of products before its P, with -D of block b + 1;
+        // then the staged elements.
         auto vector_work = [&](int k) {
-            const int rl = k - NS / 2;                        // slots NS/2 .. NS/2+3
-            if (rl >= 0 && rl < 4) {
-                lv[0][rl] = ld_rows(0, 0, rl);
-                load_nd(1, rl);
-            }
-            const int rl1 = k - (NS + NS / 2);                // block 1's L
-            if (rl1 >= 0 && rl1 < 4) lv[1][rl1] = ld_rows(0, 1, rl1);
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int start = blk ? 2 * NS : NS;          // first slot of the block's elements
-                const int E = 16 / (blk ? NG : NS);           // elements per slot
+            for (int blk = 0; blk < NB; ++blk) {
+                const int rl = k - (blk * NS + NS / 2);
+                if (rl >= 0 && rl < 4) {
+                    lv[blk % 2][rl] = ld_rows(0, blk, rl);
+                    if (blk + 1 < NB) load_nd(blk + 1, rl);
+                }
+            }
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const bool last = blk == NB - 1;
+                const int start = last ? NB * NS : (blk + 1) * NS;   // first slot of the block's elements
+                const int E = 16 / (last ? NG : NS);                 // elements per slot
                 const int t = k - start;
 #pragma unroll
                 for (int i = 0; i < E; ++i) {
@@ -1679,7 +1700,7 @@ void bwd_kv_kernel(const BwdParams p) {
             if (CAUSAL && qt0 + 32 * blk < kw0 + 31) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk][i] = -kInf;
+                    if (kv > qt0 + 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3)) sc[blk % NSB][i] = -kInf;
             }
         };
         // -D of block 0 before the first operands: its dP products start at slot 1.
@@ -1692,19 +1713,19 @@ void bwd_kv_kernel(const BwdParams p) {
             if (k + kPrefetch < NP) abuf[k % kPrefetch] = load_a(k + kPrefetch);
             product(k, a);
             vector_work(k);
-            const int jc = k - (2 * NS + NG);               // the next tile's copies: last phase
+            const int jc = k - kCopy0;                      // the next tile's copies
             if (jc >= 0 && jc < NCOPY) copy_part(cp, jc);
         };
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) abuf[k] = load_a(k);
 #pragma unroll
-        for (int k = 0; k < NS; ++k) slot(k);
-        mask(0);
+        for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
-        for (int k = NS; k < 2 * NS; ++k) slot(k);
-        mask(1);
+            for (int k = blk * NS; k < (blk + 1) * NS; ++k) slot(k);
+            mask(blk);
+        }
 #pragma unroll
-        for (int k = 2 * NS; k < NP; ++k) slot(k);
+        for (int k = NB * NS; k < NP; ++k) slot(k);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -2171,8 +2192,11 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 fn = reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>);
                 threads = 512;
             } else {
-                fn = p.bmask ? reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, true>)
-                             : reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false>);
+                // 128-row query tiles at d = 64 when every tile lies below N.
+                if (p.bmask) fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, true, 2>);
+                else if (D == 64 && p.N % 128 == 0)
+                    fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, D == 64 ? 4 : 2>);
+                else fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, 2>);
                 threads = 256;
             }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
