@@ -95,14 +95,16 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 //     one step earlier.
 //   * Within a wave the work is software-pipelined.  Step j runs the softmax
 //     of S_j (computed one step earlier) while the matrix cores compute
-//     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j while the row sums of
-//     P_j are added up, so vector and matrix work of neighbouring tiles
-//     overlap.  At d = 64 the second wave of each SIMD runs its steps half a
-//     step later (see the loop).
-//   * The running max m is raised only when a row's new max exceeds it by more
-//     than kLazyMax (log2 units).  O~, l and L all use the same m, so this is
-//     the same algebra as the method's rescale; it only bounds P by 2^kLazyMax
-//     instead of 1, and the O~ rescale becomes rare.
+//     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j, so vector and matrix
+//     work of neighbouring tiles overlap.  At d = 64 the second wave of each
+//     SIMD runs its steps half a step later (see the loop).
+//   * The reference m of the online softmax is raised only when P formed
+//     against it would leave [0, 2^16] in a tile (a tile's row sum is checked
+//     as it is formed; the row max is taken only then).  O~, l and L all use
+//     the same m, so this is the same algebra as the method's rescale; P is
+//     bounded by 2^16 instead of 1, and the per-tile row max and the O~
+//     rescale become rare.  (fwd_pipe256_kernel raises m when the row max
+//     exceeds it by more than kLazyMax.)
 constexpr float kLazyMax = 8.0f;
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -287,40 +289,49 @@ void fwd_pipe_kernel(const FwdParams p) {
     float m_run = kNegInf;   // reference max of c * S (log2 domain), equal in lanes l and l ^ 32
     float l_run = 0.f;       // this lane's half of the row sum, relative to m_run
 
-    // P = exp2(c S - m) in place (fp32, for the row sum) and packed to bf16
-    // (the B operand of the P V product); returns the rescale factor of O~ and l.
-    auto softmax = [&](f32x16 (&s)[2], uint32_t (&pp)[2][8]) -> float {
+    // P = exp2(c S - m) packed to bf16 (the B operand of the P V product),
+    // against the current reference m and summed as it is formed, without a
+    // row max in the common case: only when some lane's tile sum leaves
+    // [0, 2^16] does the tile's max raise m (and rescale O~ and l), and P is
+    // formed again.  So P stays at most 2^16 (no overflow in P, O~ or
+    // l), and the first tile, with m = -inf, always takes the max path.  S is
+    // left in place for that path.  Returns the rescale factor; lsum gets this
+    // lane's half of the tile's row sum.
+    auto softmax_nomax = [&](const f32x16 (&s)[2], uint32_t (&pp)[2][8], float& lsum) -> float {
+        constexpr float kMaxTileSum = 65536.f;
+        auto form = [&](float m_sub) {
+            float ls = 0.f;
+#pragma unroll
+            for (int bs = 0; bs < 2; ++bs)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float t0 = exp2_fast(fmaf(s[bs][r], p.c, -m_sub));
+                    const float t1 = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_sub));
+                    pp[bs][r >> 1] = pack_el(t0, t1);
+                    ls += t0 + t1;
+                }
+            return ls;
+        };
+        // With m = -inf a finite reference far below any score sends the tile
+        // to the max path (exp2 overflows); masked scores still give 0.
+        float ls = form(m_run == kNegInf ? -0x1.0p100f : m_run);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kMaxTileSum)) == 0) {
+            lsum = ls;
+            return 1.f;
+        }
         float mx = kNegInf;
 #pragma unroll
         for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bs][r]);
         mx = max_halves(mx) * p.c;
-        const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+        const float m_new = fmaxf(mx, m_run);
         const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);
         m_run = m_new;
-        // Block-sparse rows may not have seen an unmasked key yet (m = -inf):
-        // exp2(-inf - 0) = 0 then, where -inf - (-inf) would be NaN.
-        const float m_sub = SPARSE && m_new == kNegInf ? 0.f : m_new;
-#pragma unroll
-        for (int bs = 0; bs < 2; ++bs)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                s[bs][r] = exp2_fast(fmaf(s[bs][r], p.c, -m_sub));
-                s[bs][r + 1] = exp2_fast(fmaf(s[bs][r + 1], p.c, -m_sub));
-                pp[bs][r >> 1] = pack_el(s[bs][r], s[bs][r + 1]);
-            }
+        lsum = form(m_new == kNegInf ? 0.f : m_new);
         return alpha;
     };
 
-    auto row_sum = [&](const f32x16 (&pr)[2], float alpha) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int bs = 0; bs < 2; ++bs)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) lsum += pr[bs][r] + pr[bs][r + 1];
-        l_run = fmaf(l_run, alpha, lsum);
-    };
 
     // O^T += V^T P^T: V^T fragments by transposed reads of the row-major V tile
     // (rows 16*kk + 4*g + j16/4 and +8, columns 32*db + 16*half + 4*(j16 % 4)).
@@ -385,7 +396,8 @@ void fwd_pipe_kernel(const FwdParams p) {
             __builtin_amdgcn_s_setprio(1);
             if (own_next) scores(Ks, s_next);
             if (own) {
-                const float alpha = softmax(s_cur, pp);
+                float lsum;
+                const float alpha = softmax_nomax(s_cur, pp, lsum);
                 // Materialize P here, beside the S_{j+1} products, rather than
                 // letting the compiler sink the exponentials below the branch.
 #pragma unroll
@@ -398,9 +410,9 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
                 }
+                l_run = fmaf(l_run, alpha, lsum);
                 if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
                 pv(Vs, pp);
-                row_sum(s_cur, alpha);
             }
             if constexpr (SPARSE) __builtin_amdgcn_s_setprio(0);
         }
@@ -443,7 +455,8 @@ void fwd_pipe_kernel(const FwdParams p) {
         mask(j, s_cur);
         __builtin_amdgcn_s_setprio(1);
         scores(Ks, s_next);
-        const float alpha = softmax(s_cur, pp);
+        float lsum;
+        const float alpha = softmax_nomax(s_cur, pp, lsum);
 #pragma unroll
         for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
@@ -454,6 +467,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
         }
+        l_run = fmaf(l_run, alpha, lsum);
         __builtin_amdgcn_s_setprio(0);
         return alpha;
     };
@@ -468,16 +482,12 @@ void fwd_pipe_kernel(const FwdParams p) {
             copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
             if constexpr (!LATE) {
                 if (j < n_w) {
-                    const float alpha = softmax_phase(j, Ks, s_cur, s_next);
+                    softmax_phase(j, Ks, s_cur, s_next);
                     pv(Vs, pp);
-                    row_sum(s_cur, alpha);
                 }
             } else {
                 if (j >= 1 && j - 1 < n_w) pv(Vp, pp);
-                if (j < n_w) {
-                    const float alpha = softmax_phase(j, Ks, s_cur, s_next);
-                    row_sum(s_cur, alpha);
-                }
+                if (j < n_w) softmax_phase(j, Ks, s_cur, s_next);
             }
             wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
             barrier_lds();
