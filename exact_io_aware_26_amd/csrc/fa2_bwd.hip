@@ -1395,15 +1395,16 @@ void bwd_dq256_kernel(const BwdParams p) {
 // since a score accumulator register holds the 8 queries, in the order of the
 // transposed reads, that the B operand of a 16-query step needs.  Within a
 // tile, the vector work of one query block overlaps the products of the next.
-// NB query blocks per tile: 2 (64-row tiles), or 4 at d = 64 when N is a
-// multiple of 128 (128-row tiles, so a tile's fixed costs -- barrier, waits,
-// copies, the operand pipeline's restart -- spread over as many products as
-// at d = 128; the workspace rows are padded to 64 only, so the 128-row tiles
-// must not pass N).
+// NB query blocks per tile: 2 (64-row tiles), or 4 when N is a multiple of
+// 128 at d = 64 and for causal d = 128 (128-row tiles, so a tile's fixed costs
+// -- barrier, waits, copies, the operand pipeline's restart -- spread over
+// twice the products; the workspace rows are padded to 64 only, so the 128-row
+// tiles must not pass N).  At d = 128 two such tiles fill the LDS, so the ring
+// is two deep there.
 template <int D, bool CAUSAL, bool SPARSE, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_kv_kernel(const BwdParams p) {
-    static_assert(NB == 2 || (NB == 4 && D == 64 && !SPARSE), "tile shapes");
+    static_assert(NB == 2 || (NB == 4 && !SPARSE), "tile shapes");
     constexpr int NW = 4, BC = 32 * NW, BR = 32 * NB;
     constexpr int RB = 2 * D;                 // bytes per row of the Q / dO tiles
     constexpr int kTile = BR * RB;
@@ -1419,7 +1420,11 @@ void bwd_kv_kernel(const BwdParams p) {
     // below 64 KiB.
     constexpr int kBuf = 2 * kTile + 2 * BR * 4;
     static_assert(kBuf % 256 == 0, "tile arrays keep the 256-byte alignment the swizzle needs");
-    __shared__ __attribute__((aligned(256))) char Ta0[kBuf], Ta1[kBuf], Ta2[kBuf];
+    // 128-row tiles at d = 128 leave room for two buffers only: each tile's
+    // copies are then issued in its first slots, into the buffer the previous
+    // tile released, and waited for at its end.
+    constexpr int NBUF = 3 * kBuf > 160 * 1024 ? 2 : 3;
+    __shared__ __attribute__((aligned(256))) char Ta0[kBuf], Ta1[kBuf], Ta2[NBUF == 3 ? kBuf : 256];
     FA2_LDS char* const T0 = (FA2_LDS char*)Ta0;
     FA2_LDS char* const T1 = (FA2_LDS char*)Ta1;
     FA2_LDS char* const T2 = (FA2_LDS char*)Ta2;
@@ -1582,7 +1587,7 @@ void bwd_kv_kernel(const BwdParams p) {
     static_assert(NCOPY <= NB * NG, "the copies of the next tile fit in the dV, dK phases");
     // The next tile's copies take the last slots of the last dV, dK phase (and
     // of the one before it when they do not fit).
-    constexpr int kCopy0 = NB * NS + (NB - 1) * NG - (NCOPY > NG ? NCOPY - NG : 0);
+    constexpr int kCopy0 = NBUF == 2 ? 0 : NB * NS + (NB - 1) * NG - (NCOPY > NG ? NCOPY - NG : 0);
     constexpr int NSB = NB > 2 ? 3 : 2;       // score buffers
     auto tile = [&](const FA2_LDS char* T, int qt0, const TileCopy& cp) {
         // Lane bases with the tile's address folded in, rebuilt per tile (opaque
@@ -1732,21 +1737,29 @@ void bwd_kv_kernel(const BwdParams p) {
     auto step = [&](int it, const FA2_LDS char* T, FA2_LDS char* Tw) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        tile(T, qrow_at(it % n_i), plan_copy(min(it + 2, n_iter - 1), Tw));
-        wait_vm_keep<NCOPY>();          // tile it+1, issued one step earlier, has landed
+        tile(T, qrow_at(it % n_i), plan_copy(min(it + NBUF - 1, n_iter - 1), Tw));
+        if constexpr (NBUF == 3) wait_vm_keep<NCOPY>();   // tile it+1, issued one step earlier, has landed
+        else wait_vm_all();                                // tile it+1, issued at this step's start
         barrier_lds();
     };
 
     if (n_iter > 0) {
         copy_tile(0, T0);
-        if (n_iter > 1) copy_tile(1, T1);
+        if (NBUF == 3 && n_iter > 1) copy_tile(1, T1);
         wait_vm_all();
         __syncthreads();
-        for (int it = 0; it < n_iter; it += 3) {
-            step(it, T0, T2);
-            if (it + 1 < n_iter) {
-                step(it + 1, T1, T0);
-                if (it + 2 < n_iter) step(it + 2, T2, T1);
+        if constexpr (NBUF == 3) {
+            for (int it = 0; it < n_iter; it += 3) {
+                step(it, T0, T2);
+                if (it + 1 < n_iter) {
+                    step(it + 1, T1, T0);
+                    if (it + 2 < n_iter) step(it + 2, T2, T1);
+                }
+            }
+        } else {
+            for (int it = 0; it < n_iter; it += 2) {
+                step(it, T0, T1);
+                if (it + 1 < n_iter) step(it + 1, T1, T0);
             }
         }
         wait_vm_all();
@@ -2192,10 +2205,11 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 fn = reinterpret_cast<const void*>(&bwd_pair_kernel<D, CAUSAL, true>);
                 threads = 512;
             } else {
-                // 128-row query tiles at d = 64 when every tile lies below N.
+                // 128-row query tiles when every tile lies below N, at d = 64 and
+                // for causal d = 128 (non-causal d = 128 ran slower with them).
                 if (p.bmask) fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, true, 2>);
-                else if (D == 64 && p.N % 128 == 0)
-                    fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, D == 64 ? 4 : 2>);
+                else if ((D == 64 || CAUSAL) && p.N % 128 == 0)
+                    fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, (D == 64 || CAUSAL) ? 4 : 2>);
                 else fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, 2>);
                 threads = 256;
             }
