@@ -318,7 +318,7 @@ fa2_status fwd_impl(bool f16, bool sparse, const unsigned char* bmask, const voi
     p.Hkv = Hkv;
     p.N = N;
     p.G = Hq / Hkv;
-    p.n_qtiles = (N + fa2::kFwdRows - 1) / fa2::kFwdRows;
+    p.n_qtiles = 0;     // set by the launcher for its workgroup shape
     p.c = (float)((double)scale * kLog2e);
     p.bmask = sparse ? bmask : nullptr;
     p.nb = (N + fa2::kSparseBlock - 1) / fa2::kSparseBlock;

@@ -82,9 +82,13 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
         }
 }
 
-// Pipelined forward for d = 64 and 128: one workgroup = 8 wave64s = 256 query
-// rows (two waves per SIMD), so each K/V tile brought into LDS serves twice
-// as many rows as a 4-wave workgroup would.
+// Pipelined forward for d = 64 and 128: one workgroup = NW wave64s of 32 query
+// rows each.  At d = 128 (and for block-sparse attention) NW = 8: 256 rows, two
+// waves per SIMD, so each K/V tile brought into LDS serves twice as many rows
+// as a 4-wave workgroup would.  Dense d = 64 takes NW = 4 (128 rows, 165
+// registers, 48 KiB of LDS) with three workgroups resident per CU, i.e. three
+// waves per SIMD from independent workgroups: each wave's waits and barriers
+// are then covered by two others (+5-11 % over one 8-wave workgroup per CU).
 //   * K/V tiles are copied from global memory straight into LDS
 //     (global_load_lds_dwordx4, no staging registers), K one tile ahead of V:
 //     during step j the waves read K_{j+1} and V_j while K_{j+3} and V_{j+2}
@@ -96,8 +100,9 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 //   * Within a wave the work is software-pipelined.  Step j runs the softmax
 //     of S_j (computed one step earlier) while the matrix cores compute
 //     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j, so vector and matrix
-//     work of neighbouring tiles overlap.  At d = 64 the second wave of each
-//     SIMD runs its steps half a step later (see the loop).
+//     work of neighbouring tiles overlap.  In the 8-wave kernel at d = 64
+//     (block-sparse) the second wave of each SIMD runs its steps half a step
+//     later (see the loop).
 //   * The reference m of the online softmax is raised only when P formed
 //     against it would leave [0, 2^16] in a tile (a tile's row sum is checked
 //     as it is formed; the row max is taken only then).  O~, l and L all use
@@ -107,10 +112,12 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 //     exceeds it by more than kLazyMax.)
 constexpr float kLazyMax = 8.0f;
 
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, bool SPARSE, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(NW == 4 ? 3 : 2, NW == 4 ? 3 : 2)))
 void fwd_pipe_kernel(const FwdParams p) {
-    constexpr int NW = 8, ROWS = 32 * NW, BC = 64;
+    static_assert(NW == 8 || (NW == 4 && D == 64 && !SPARSE), "workgroup shapes");
+    constexpr int ROWS = 32 * NW, BC = 64;
     constexpr int KSD = D / 16;          // MFMA reduction steps over the head dim
     constexpr int NBD = D / 32;          // 32-wide blocks of the head dim (O^T)
     constexpr int RB = 2 * D;            // bytes per LDS tile row
@@ -121,7 +128,7 @@ void fwd_pipe_kernel(const FwdParams p) {
     static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
     // At d = 64 the two waves of a SIMD run half a step apart (see the loop
     // below), which needs a fourth V buffer; K gets one too for a period-4 ring.
-    constexpr bool kPingPong = D == 64;
+    constexpr bool kPingPong = D == 64 && NW == 8;
     constexpr int kTile3 = kPingPong ? kTile : 16;
     __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile], Kb3[kTile3];
     __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile], Vb3[kTile3];
@@ -438,7 +445,8 @@ void fwd_pipe_kernel(const FwdParams p) {
     // (P_{j-1} V_{j-1}, then S_{j+1} with the softmax of S_j): while one wave
     // of a SIMD does its vector-heavy half the other issues matrix products.
     // This pays at d = 64, where the vector work per product is twice that of
-    // d = 128 (at d = 128 the extra live registers cost more than it gains).
+    // d = 128 (at d = 128 the extra live registers cost more than it gains);
+    // only the 8-wave (block-sparse) d = 64 kernel runs it.
     // K and V tiles live in four-buffer rings (tile t in buffer t % 4): step j
     // reads K_{j+1}, V_j and V_{j-1}, and copies K_{j+3} and V_{j+2} into the
     // buffers of K_{j-1} and V_{j-2}, which no wave reads after step j - 1.
@@ -868,11 +876,17 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     FwdParams arg = p;
     void* args[] = {&arg};
     if constexpr (D <= 128) {
-        arg.n_qtiles = (p.N + 255) / 256;
+        // Dense d = 64: 128-row workgroups of 4 waves, three per CU (3 waves per
+        // SIMD); otherwise 256 rows, 8 waves, one per CU.
+        const bool small = D == 64 && !p.bmask;
+        const int rows = small ? 128 : 256;
+        arg.n_qtiles = (p.N + rows - 1) / rows;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
-        const void* fn = p.bmask ? reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true>)
-                                 : reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false>);
-        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512), args, 0, stream);
+        const void* fn;
+        if (p.bmask) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true, 8>);
+        else if constexpr (D == 64) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 4>);
+        else fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 8>);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(2 * rows), args, 0, stream);
     } else {
         arg.n_qtiles = (p.N + 127) / 128;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;

@@ -52,9 +52,6 @@ struct BwdParams {
 // the K/V-tile loop), so that whole tiles of L and D can be copied unchecked.
 constexpr int kBwdRowPad = 64;
 
-// Rows of Q per forward workgroup (the grid is B * Hq * ceil(N / kFwdRows)).
-constexpr int kFwdRows = 128;
-
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
 // stages: bit 0 preprocess (D; zeroes the dQ accumulator in atomic mode), bit 1 the K/V-tile
 // loop (dK, dV; plus dQ atomics in atomic mode), bit 2 dQ (its own pass, or the
@@ -69,7 +66,6 @@ namespace fa2_f16 {
 using fa2::BwdParams;
 using fa2::FwdParams;
 using fa2::kBwdRowPad;
-using fa2::kFwdRows;
 using fa2::kSparseBlock;
 using fa2::kSparseMaxN;
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
