@@ -83,20 +83,22 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 }
 
 // Pipelined forward for d = 64 and 128: one workgroup = NW wave64s of 32 query
-// rows each.  At d = 128 (and for block-sparse attention) NW = 8: 256 rows, two
-// waves per SIMD, so each K/V tile brought into LDS serves twice as many rows
-// as a 4-wave workgroup would.  Dense d = 64 takes NW = 4 (128 rows, 165
-// registers, 48 KiB of LDS) with three workgroups resident per CU, i.e. three
-// waves per SIMD from independent workgroups: each wave's waits and barriers
-// are then covered by two others (+5-11 % over one 8-wave workgroup per CU).
+// rows each.  Dense attention takes NW = 4 (128 rows) with several workgroups
+// resident per CU, so the waves sharing a SIMD come from independent
+// workgroups and cover each other's waits and barriers: at d = 64 three per CU
+// (165 registers, 48 KiB of LDS; three waves per SIMD, +5-11 % over one 8-wave
+// workgroup per CU), at d = 128 two per CU (250 registers; two-deep K/V rings
+// of 64 KiB; +2-5 %).  Block-sparse attention takes NW = 8 (256 rows, two
+// mask blocks), one workgroup per CU.
 //   * K/V tiles are copied from global memory straight into LDS
 //     (global_load_lds_dwordx4, no staging registers), K one tile ahead of V:
 //     during step j the waves read K_{j+1} and V_j while K_{j+3} and V_{j+2}
-//     are in flight.  The buffers (three per tensor at d = 128, four at
-//     d = 64) are distinct LDS objects and the loop is unrolled by the ring
-//     period, so no read names the buffer being filled and the compiler adds
-//     no wait on in-flight tiles; each step waits only for the copies issued
-//     one step earlier.
+//     are in flight (three buffers per tensor; four in the 8-wave d = 64
+//     kernel), or K_{j+2} and V_{j+1} (two buffers, 4-wave d = 128 kernel).
+//     The buffers are distinct LDS objects and the loop is unrolled by the
+//     ring period, so no read names the buffer being filled and the compiler
+//     adds no wait on in-flight tiles; with three buffers each step waits only
+//     for the copies issued one step earlier, with two for its own.
 //   * Within a wave the work is software-pipelined.  Step j runs the softmax
 //     of S_j (computed one step earlier) while the matrix cores compute
 //     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j, so vector and matrix
@@ -114,9 +116,9 @@ constexpr float kLazyMax = 8.0f;
 
 template <int D, bool CAUSAL, bool SPARSE, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(NW == 4 ? 3 : 2, NW == 4 ? 3 : 2)))
+                          amdgpu_waves_per_eu(NW == 4 && D == 64 ? 3 : 2, NW == 4 && D == 64 ? 3 : 2)))
 void fwd_pipe_kernel(const FwdParams p) {
-    static_assert(NW == 8 || (NW == 4 && D == 64 && !SPARSE), "workgroup shapes");
+    static_assert(NW == 8 || (NW == 4 && !SPARSE), "workgroup shapes");
     constexpr int ROWS = 32 * NW, BC = 64;
     constexpr int KSD = D / 16;          // MFMA reduction steps over the head dim
     constexpr int NBD = D / 32;          // 32-wide blocks of the head dim (O^T)
@@ -129,9 +131,14 @@ void fwd_pipe_kernel(const FwdParams p) {
     // At d = 64 the two waves of a SIMD run half a step apart (see the loop
     // below), which needs a fourth V buffer; K gets one too for a period-4 ring.
     constexpr bool kPingPong = D == 64 && NW == 8;
+    // K/V ring depth: three tiles per tensor, or two for 4-wave workgroups at
+    // d = 128 (64 KiB, two workgroups per CU), whose steps issue their copies
+    // at the start and wait for them at the end.
+    constexpr int NRING = D == 128 && NW == 4 ? 2 : 3;
+    constexpr int kTile2 = NRING == 3 ? kTile : 16;
     constexpr int kTile3 = kPingPong ? kTile : 16;
-    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile], Kb3[kTile3];
-    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile], Vb3[kTile3];
+    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile2], Kb3[kTile3];
+    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile2], Vb3[kTile3];
     FA2_LDS char* const K0 = (FA2_LDS char*)Kb0;
     FA2_LDS char* const K1 = (FA2_LDS char*)Kb1;
     FA2_LDS char* const K2 = (FA2_LDS char*)Kb2;
@@ -369,9 +376,9 @@ void fwd_pipe_kernel(const FwdParams p) {
     copy_tile(Vh, tile_at(0), V0);
     if (1 < n_kv) {
         copy_tile(Kh, tile_at(1), K1);
-        copy_tile(Vh, tile_at(1), V1);
+        if (NRING == 3) copy_tile(Vh, tile_at(1), V1);
     }
-    if (2 < n_kv) copy_tile(Kh, tile_at(2), K2);
+    if (NRING == 3 && 2 < n_kv) copy_tile(Kh, tile_at(2), K2);
     wait_vm_all();
     __syncthreads();
     f32x16 sa[2], sb[2];       // scores of the current and the next tile, alternating
@@ -387,8 +394,8 @@ void fwd_pipe_kernel(const FwdParams p) {
                     f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
         // Copies past the last tile repeat it into a released buffer that is
         // never read, so every step issues and waits for the same count.
-        copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
-        copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
+        copy_tile(Kh, tile_at(min(j + NRING, n_kv - 1)), Kw);
+        copy_tile(Vh, tile_at(min(j + NRING - 1, n_kv - 1)), Vw);
         if (j < n_w) {
             // Block-sparse: no work on a tile this wave's mask block does not
             // need, neither its softmax and P V products (step j) nor its
@@ -423,10 +430,17 @@ void fwd_pipe_kernel(const FwdParams p) {
             }
             if constexpr (SPARSE) __builtin_amdgcn_s_setprio(0);
         }
-        wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
+        if constexpr (NRING == 3) wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
+        else wait_vm_all();                                 // K_{j+2} and V_{j+1}, issued at this step's start
         barrier_lds();
     };
 
+    if constexpr (NRING == 2) {
+        for (int j = 0; j < n_kv; j += 2) {
+            step(j, K1, V0, K0, V1, sa, sb);
+            if (j + 1 < n_kv) step(j + 1, K0, V1, K1, V0, sb, sa);
+        }
+    } else
     // Unrolled by six: three buffer phases times two score arrays.  Each step
     // after the first is guarded on its own rather than leaving the loop with
     // a break: with six exits the compiler copied the score arrays into fixed
@@ -876,16 +890,14 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     FwdParams arg = p;
     void* args[] = {&arg};
     if constexpr (D <= 128) {
-        // Dense d = 64: 128-row workgroups of 4 waves, three per CU (3 waves per
-        // SIMD); otherwise 256 rows, 8 waves, one per CU.
-        const bool small = D == 64 && !p.bmask;
-        const int rows = small ? 128 : 256;
+        // Dense: 128-row workgroups of 4 waves (three per CU at d = 64, two at
+        // d = 128); block-sparse: 256 rows, 8 waves, one per CU.
+        const int rows = p.bmask ? 256 : 128;
         arg.n_qtiles = (p.N + rows - 1) / rows;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
         const void* fn;
         if (p.bmask) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true, 8>);
-        else if constexpr (D == 64) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 4>);
-        else fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 8>);
+        else fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 4>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(2 * rows), args, 0, stream);
     } else {
         arg.n_qtiles = (p.N + 127) / 128;
