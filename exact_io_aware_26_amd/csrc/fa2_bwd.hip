@@ -730,8 +730,10 @@ void bwd_pair_kernel(const BwdParams p) {
 // bwd_dq_pipe: the dQ pass for d = 64 and 128.
 //
 // One workgroup = 4 wave64s, one wave per SIMD; each wave owns two 32-row query
-// blocks (u = 0, 1; 256 rows per workgroup; with a block mask one block, so
-// that a 128-row workgroup is one mask row).  Q and dO of its rows are MFMA B
+// blocks (u = 0, 1; 256 rows per workgroup) at d = 128.  With a block mask it
+// owns one block, so that a 128-row workgroup is one mask row; at d = 64 also
+// one block, so that the kernel fits 256 registers and two workgroups share a
+// CU (two waves per SIMD from independent workgroups: 3-9 % faster there).  Q and dO of its rows are MFMA B
 // operands in registers and its dQ^T accumulators stay in registers, all
 // transposed so that each lane owns one query row of each block:
 //     s  = K Q^T,  dp = V dO^T          (A: K / V rows from LDS)
@@ -751,11 +753,12 @@ void bwd_pair_kernel(const BwdParams p) {
 // buffer offset is a compile-time immediate.  The dQ^T accumulators (128
 // registers at d = 128) live in AGPRs.
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void bwd_dq_pipe_kernel(const BwdParams p) {
     // Block-sparse: one query block per wave, so a workgroup (128 rows) is
     // one mask row and computes no tile that its rows do not need.
-    constexpr int NW = 4, U = SPARSE ? 1 : 2, BRQ = 32 * U * NW, BT = 64;
+    constexpr int NW = 4, U = SPARSE || D == 64 ? 1 : 2, BRQ = 32 * U * NW, BT = 64;
     constexpr int RB = 2 * D;
     constexpr int kTile = BT * RB;
     constexpr int KSD = D / 16, NBD = D / 32;
@@ -1380,8 +1383,8 @@ void bwd_dq256_kernel(const BwdParams p) {
 // bwd_kv: the K/V-tile loop for d = 64 and 128 (dQ in its own pass).
 //
 // One workgroup = 4 wave64s = 128 keys; wave w owns keys 32w..32w+31 and the
-// whole head dim of their dK and dV, accumulated in registers (one wave per
-// SIMD with the full register file).  Query tiles of 64 rows -- Q, dO, and
+// whole head dim of their dK and dV, accumulated in registers (at d = 128 one
+// wave per SIMD with the full register file; at d = 64 two workgroups per CU).  Query tiles of 64 rows -- Q, dO, and
 // the L log2(e) and D rows of the workspace -- are copied into LDS with
 // global_load_lds, three tiles deep, in nine distinct LDS arrays with the loop
 // unrolled by three (no read names a buffer in flight; each step waits only
@@ -1395,14 +1398,17 @@ void bwd_dq256_kernel(const BwdParams p) {
 // since a score accumulator register holds the 8 queries, in the order of the
 // transposed reads, that the B operand of a 16-query step needs.  Within a
 // tile, the vector work of one query block overlaps the products of the next.
-// NB query blocks per tile: 2 (64-row tiles), or 4 when N is a multiple of
-// 128 at d = 64 and for causal d = 128 (128-row tiles, so a tile's fixed costs
-// -- barrier, waits, copies, the operand pipeline's restart -- spread over
-// twice the products; the workspace rows are padded to 64 only, so the 128-row
-// tiles must not pass N).  At d = 128 two such tiles fill the LDS, so the ring
-// is two deep there.
+// NB query blocks per tile: 2 (64-row tiles), or 4 for causal d = 128 when N
+// is a multiple of 128 (128-row tiles, so a tile's fixed costs -- barrier,
+// waits, copies, the operand pipeline's restart -- spread over twice the
+// products; the workspace rows are padded to 64 only, so the 128-row tiles
+// must not pass N).  Two such tiles fill the LDS, so the ring is two deep
+// there.  At d = 64 the kernel fits 256 registers and runs two workgroups per
+// CU (two waves per SIMD from independent workgroups), which beat 128-row
+// tiles at one wave per SIMD by 3-6 %.
 template <int D, bool CAUSAL, bool SPARSE, int NB>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 64 && NB == 2 ? 2 : 1, D == 64 && NB == 2 ? 2 : 1)))
 void bwd_kv_kernel(const BwdParams p) {
     static_assert(NB == 2 || (NB == 4 && !SPARSE), "tile shapes");
     constexpr int NW = 4, BC = 32 * NW, BR = 32 * NB;
@@ -2208,13 +2214,13 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                 // 128-row query tiles when every tile lies below N, at d = 64 and
                 // for causal d = 128 (non-causal d = 128 ran slower with them).
                 if (p.bmask) fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, true, 2>);
-                else if ((D == 64 || CAUSAL) && p.N % 128 == 0)
-                    fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, (D == 64 || CAUSAL) ? 4 : 2>);
+                else if (D == 128 && CAUSAL && p.N % 128 == 0)
+                    fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, D == 128 && CAUSAL ? 4 : 2>);
                 else fn = reinterpret_cast<const void*>(&bwd_kv_kernel<D, CAUSAL, false, 2>);
                 threads = 256;
             }
             grid = (long)p.B * p.Hkv * ((p.N + 127) / 128);
-            if (!atomic_dq) grid = std::min<long>(grid, persistent_workgroups(1));
+            if (!atomic_dq) grid = std::min<long>(grid, persistent_workgroups(D == 64 ? 2 : 1));
         } else if (atomic_dq) {
             fn = reinterpret_cast<const void*>(&bwd_main_kernel<D, CAUSAL, true>);
             constexpr int BC = BwdCfg<D>::BC;
@@ -2237,7 +2243,7 @@ hipError_t launch_bwd_t(const BwdParams& p, unsigned stages, hipStream_t stream)
                                    dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0, stream);
         }
         void* args[] = {&arg};
-        const int rows_per_wg = D <= 128 && !p.bmask ? 256 : 128;   // block-sparse: one mask row
+        const int rows_per_wg = D == 128 && !p.bmask ? 256 : 128;   // block-sparse: one mask row
         const long grid = (long)p.B * p.Hq * ((p.N + rows_per_wg - 1) / rows_per_wg);
         const void* fn;
         if constexpr (D <= 128)
