@@ -82,19 +82,20 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
         }
 }
 
-// Pipelined forward for d = 64 and 128: one workgroup = NW wave64s of 32 query
-// rows each.  Dense attention takes NW = 4 (128 rows) with several workgroups
-// resident per CU, so the waves sharing a SIMD come from independent
-// workgroups and cover each other's waits and barriers: at d = 64 three per CU
-// (165 registers, 48 KiB of LDS; three waves per SIMD, +5-11 % over one 8-wave
-// workgroup per CU), at d = 128 two per CU (250 registers; two-deep K/V rings
-// of 64 KiB; +2-5 %).  Block-sparse attention takes NW = 8 (256 rows, two
-// mask blocks), one workgroup per CU.
+// Pipelined forward for d = 64 and 128: one workgroup = 4 wave64s of 32 query
+// rows each (128 rows, one mask block of block-sparse attention), with several
+// workgroups resident per CU, so the waves sharing a SIMD come from
+// independent workgroups and cover each other's waits and barriers: at d = 64
+// three per CU (165 registers, 48 KiB of LDS; three waves per SIMD; two for
+// block-sparse, with its tile list), at d = 128 two per CU (250 registers;
+// two-deep K/V rings of 64 KiB).  Against one
+// 8-wave, 256-row workgroup per CU this ran 2-8 % faster dense and 8-30 %
+// faster block-sparse.
 //   * K/V tiles are copied from global memory straight into LDS
 //     (global_load_lds_dwordx4, no staging registers), K one tile ahead of V:
 //     during step j the waves read K_{j+1} and V_j while K_{j+3} and V_{j+2}
-//     are in flight (three buffers per tensor; four in the 8-wave d = 64
-//     kernel), or K_{j+2} and V_{j+1} (two buffers, 4-wave d = 128 kernel).
+//     are in flight (three buffers per tensor, d = 64), or K_{j+2} and
+//     V_{j+1} (two buffers, d = 128).
 //     The buffers are distinct LDS objects and the loop is unrolled by the
 //     ring period, so no read names the buffer being filled and the compiler
 //     adds no wait on in-flight tiles; with three buffers each step waits only
@@ -102,9 +103,7 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 //   * Within a wave the work is software-pipelined.  Step j runs the softmax
 //     of S_j (computed one step earlier) while the matrix cores compute
 //     S_{j+1} = K_{j+1} Q^T, then the products P_j V_j, so vector and matrix
-//     work of neighbouring tiles overlap.  In the 8-wave kernel at d = 64
-//     (block-sparse) the second wave of each SIMD runs its steps half a step
-//     later (see the loop).
+//     work of neighbouring tiles overlap.
 //   * The reference m of the online softmax is raised only when P formed
 //     against it would leave [0, 2^16] in a tile (a tile's row sum is checked
 //     as it is formed; the row max is taken only then).  O~, l and L all use
@@ -114,12 +113,11 @@ __device__ __forceinline__ void store_o_row(uint16_t* Orow, uint16_t* Olorow, co
 //     exceeds it by more than kLazyMax.)
 constexpr float kLazyMax = 8.0f;
 
-template <int D, bool CAUSAL, bool SPARSE, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(NW == 4 && D == 64 ? 3 : 2, NW == 4 && D == 64 ? 3 : 2)))
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 64 && !SPARSE ? 3 : 2, D == 64 && !SPARSE ? 3 : 2)))
 void fwd_pipe_kernel(const FwdParams p) {
-    static_assert(NW == 8 || (NW == 4 && !SPARSE), "workgroup shapes");
-    constexpr int ROWS = 32 * NW, BC = 64;
+    constexpr int NW = 4, ROWS = 32 * NW, BC = 64;
     constexpr int KSD = D / 16;          // MFMA reduction steps over the head dim
     constexpr int NBD = D / 32;          // 32-wide blocks of the head dim (O^T)
     constexpr int RB = 2 * D;            // bytes per LDS tile row
@@ -128,17 +126,13 @@ void fwd_pipe_kernel(const FwdParams p) {
     constexpr int CPR = RB / 16;         // 16-byte chunks per row
     constexpr int PERW = kTile / 1024 / NW;
     static_assert(PERW >= 1 && kTile % (1024 * NW) == 0, "tile / waves mismatch");
-    // At d = 64 the two waves of a SIMD run half a step apart (see the loop
-    // below), which needs a fourth V buffer; K gets one too for a period-4 ring.
-    constexpr bool kPingPong = D == 64 && NW == 8;
-    // K/V ring depth: three tiles per tensor, or two for 4-wave workgroups at
-    // d = 128 (64 KiB, two workgroups per CU), whose steps issue their copies
-    // at the start and wait for them at the end.
-    constexpr int NRING = D == 128 && NW == 4 ? 2 : 3;
+    // K/V ring depth: three tiles per tensor at d = 64 (48 KiB, three
+    // workgroups per CU), two at d = 128 (64 KiB, two per CU), whose steps
+    // issue their copies at their start and wait for them at their end.
+    constexpr int NRING = D == 128 ? 2 : 3;
     constexpr int kTile2 = NRING == 3 ? kTile : 16;
-    constexpr int kTile3 = kPingPong ? kTile : 16;
-    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile2], Kb3[kTile3];
-    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile2], Vb3[kTile3];
+    __shared__ __attribute__((aligned(16))) char Kb0[kTile], Kb1[kTile], Kb2[kTile2];
+    __shared__ __attribute__((aligned(16))) char Vb0[kTile], Vb1[kTile], Vb2[kTile2];
     FA2_LDS char* const K0 = (FA2_LDS char*)Kb0;
     FA2_LDS char* const K1 = (FA2_LDS char*)Kb1;
     FA2_LDS char* const K2 = (FA2_LDS char*)Kb2;
@@ -179,28 +173,22 @@ void fwd_pipe_kernel(const FwdParams p) {
 
     // Tiles the workgroup streams, and tiles this wave computes on.
     //   Dense: tiles 0 .. n_kv-1 (causal: up to the workgroup's last row).
-    //   Block-sparse: the list entries 0 .. n_kv-1, the tiles of every key
-    //   block that either of the workgroup's two 128-row mask blocks needs
-    //   (its mask byte is set and, when causal, the block starts at or below
-    //   the mask block's last row), each entry flagged with the mask blocks
-    //   that need it.  A wave computes every entry up to its own causal limit
-    //   and masks the tiles its own mask block does not need, so the
-    //   score-ahead pipeline below stays the dense one.
+    //   Block-sparse: the workgroup's 128 rows are one mask block; the list
+    //   entries 0 .. n_kv-1 are the tiles of every key block its mask row
+    //   keeps (causal: the blocks at or below the diagonal).  A wave computes
+    //   every entry up to its own causal limit, so the score-ahead pipeline
+    //   below stays the dense one.
     int n_kv, n_w;
     FA2_LDS uint16_t* tl = nullptr;
     if constexpr (SPARSE) {
-        static_assert(ROWS == 2 * kSparseBlock && 2 * BC == kSparseBlock, "two mask blocks, two tiles per block");
+        static_assert(ROWS == kSparseBlock && 2 * BC == kSparseBlock, "one mask block, two tiles per block");
         __shared__ uint16_t tl_arr[kSparseMaxN / BC];
         __shared__ int tl_count;
         tl = (FA2_LDS uint16_t*)tl_arr;
         if (wave == 0) {
             const int r0 = q0 / kSparseBlock, nb = p.nb;
-            const bool has1 = q0 + kSparseBlock < N;
             const int n = build_tile_list(tl, nb, (N + BC - 1) / BC, lane, [&](int c) {
-                int f = 0;
-                if (p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0)) f |= 1;
-                if (has1 && p.bmask[(size_t)(r0 + 1) * nb + c] != 0 && (!CAUSAL || c <= r0 + 1)) f |= 2;
-                return f;
+                return p.bmask[(size_t)r0 * nb + c] != 0 && (!CAUSAL || c <= r0) ? 1 : 0;
             });
             if (lane == 0) tl_count = n;
         }
@@ -216,14 +204,10 @@ void fwd_pipe_kernel(const FwdParams p) {
         n_kv = CAUSAL ? (min(q0 + ROWS, N) - 1) / BC + 1 : (N + BC - 1) / BC;
         n_w = wq0 >= N ? 0 : CAUSAL ? min(wq0 + 31, N - 1) / BC + 1 : n_kv;
     }
-    // Key tile of step j, and (block-sparse) whether this wave's mask block needs it.
+    // Key tile of step j.
     auto tile_at = [&](int j) -> int {
         if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)(tl[j] & 0xfff));
         else return j;
-    };
-    auto own_at = [&](int j) -> bool {
-        if constexpr (SPARSE) return ((__builtin_amdgcn_readfirstlane((int)tl[j]) >> (12 + (wave >> 2))) & 1) != 0;
-        else return true;
     };
 
     // Copy tile t of K or V into LDS.  Lane i of a copy instruction writes
@@ -279,12 +263,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 
     auto mask = [&](int j, f32x16 (&s)[2]) {
         const int kv0 = tile_at(j) * BC;
-        if (!own_at(j)) {
-#pragma unroll
-            for (int bs = 0; bs < 2; ++bs)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[bs][r] = kNegInf;
-        } else if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
+        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0)) {
             // Element (bs, r) holds key kv0 + 4g + off with off a constant; it
             // is masked when the key exceeds min(q, N - 1) (causal) or N - 1,
             // i.e. when off > lim: one compare and one select per element.
@@ -385,7 +364,7 @@ void fwd_pipe_kernel(const FwdParams p) {
     scores(K0, sa);
     __syncthreads();          // K_0 is overwritten by K_3 in step 0
 
-    if constexpr (!kPingPong) {
+    {
     // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
     // then P_j V_j.  Past a wave's last tile the step only copies; S_{j+1} of a
     // tile the wave does not visit is computed from whatever its buffer holds
@@ -397,19 +376,17 @@ void fwd_pipe_kernel(const FwdParams p) {
         copy_tile(Kh, tile_at(min(j + NRING, n_kv - 1)), Kw);
         copy_tile(Vh, tile_at(min(j + NRING - 1, n_kv - 1)), Vw);
         if (j < n_w) {
-            // Block-sparse: no work on a tile this wave's mask block does not
-            // need, neither its softmax and P V products (step j) nor its
-            // scores (computed one step ahead, in step j - 1).
-            const bool own = !SPARSE || own_at(j);
-            const bool own_next = !SPARSE || (j + 1 < n_w && own_at(j + 1));
-            if (own) mask(j, s_cur);
+            // Block-sparse: no scores for a list entry past this wave's last
+            // (computed one step ahead, in step j - 1).
+            const bool own_next = !SPARSE || j + 1 < n_w;
+            mask(j, s_cur);
             uint32_t pp[2][8];
             // Raised priority while this wave interleaves S_{j+1} with the
             // softmax of S_j, normal for the P V products: the other wave on the
             // SIMD then fills the matrix unit's idle slots of the mixed phase.
             __builtin_amdgcn_s_setprio(1);
             if (own_next) scores(Ks, s_next);
-            if (own) {
+            {
                 float lsum;
                 const float alpha = softmax_nomax(s_cur, pp, lsum);
                 // Materialize P here, beside the S_{j+1} products, rather than
@@ -425,10 +402,9 @@ void fwd_pipe_kernel(const FwdParams p) {
                         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
                 }
                 l_run = fmaf(l_run, alpha, lsum);
-                if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_s_setprio(0);
                 pv(Vs, pp);
             }
-            if constexpr (SPARSE) __builtin_amdgcn_s_setprio(0);
         }
         if constexpr (NRING == 3) wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
         else wait_vm_all();                                 // K_{j+2} and V_{j+1}, issued at this step's start
@@ -453,84 +429,6 @@ void fwd_pipe_kernel(const FwdParams p) {
         if (j + 4 < n_kv) step(j + 4, K2, V1, K1, V0, sa, sb);
         if (j + 5 < n_kv) step(j + 5, K0, V2, K2, V1, sb, sa);
     }
-    } else {
-    // Waves w and w + 4 share a SIMD.  Waves 0-3 run each step as (S_{j+1}
-    // with the softmax of S_j, then P_j V_j), waves 4-7 half a step later as
-    // (P_{j-1} V_{j-1}, then S_{j+1} with the softmax of S_j): while one wave
-    // of a SIMD does its vector-heavy half the other issues matrix products.
-    // This pays at d = 64, where the vector work per product is twice that of
-    // d = 128 (at d = 128 the extra live registers cost more than it gains);
-    // only the 8-wave (block-sparse) d = 64 kernel runs it.
-    // K and V tiles live in four-buffer rings (tile t in buffer t % 4): step j
-    // reads K_{j+1}, V_j and V_{j-1}, and copies K_{j+3} and V_{j+2} into the
-    // buffers of K_{j-1} and V_{j-2}, which no wave reads after step j - 1.
-    FA2_LDS char* const K3 = (FA2_LDS char*)Kb3;
-    FA2_LDS char* const V3 = (FA2_LDS char*)Vb3;
-    const bool late = wave >= 4;
-    uint32_t pp[2][8];         // P_j packed to bf16 (the late waves keep it for the next step)
-    // S_{j+1} beside the softmax of S_j.  (Block-sparse tiles this wave's
-    // mask block does not need are masked to -inf here rather than skipped:
-    // a branch between the products and the softmax costs this kernel more
-    // than the skipped work saves.)
-    auto softmax_phase = [&](int j, const FA2_LDS char* Ks, f32x16 (&s_cur)[2], f32x16 (&s_next)[2])
-        __attribute__((always_inline)) -> float {
-        mask(j, s_cur);
-        __builtin_amdgcn_s_setprio(1);
-        scores(Ks, s_next);
-        float lsum;
-        const float alpha = softmax_nomax(s_cur, pp, lsum);
-#pragma unroll
-        for (int bs = 0; bs < 2; ++bs)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(pp[bs][r]));
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-            for (int i = 0; i < NBD; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-        }
-        l_run = fmaf(l_run, alpha, lsum);
-        __builtin_amdgcn_s_setprio(0);
-        return alpha;
-    };
-    // The loop is instantiated once per wave group (LATE = the late waves), so
-    // each group's registers are allocated for its own program.
-    auto run = [&](auto late_tag) __attribute__((always_inline)) {
-        constexpr bool LATE = decltype(late_tag)::value;
-        auto step = [&](int j, const FA2_LDS char* Ks, const FA2_LDS char* Vs, const FA2_LDS char* Vp,
-                        FA2_LDS char* Kw, FA2_LDS char* Vw, f32x16 (&s_cur)[2], f32x16 (&s_next)[2])
-            __attribute__((always_inline)) {
-            copy_tile(Kh, tile_at(min(j + 3, n_kv - 1)), Kw);
-            copy_tile(Vh, tile_at(min(j + 2, n_kv - 1)), Vw);
-            if constexpr (!LATE) {
-                if (j < n_w) {
-                    softmax_phase(j, Ks, s_cur, s_next);
-                    pv(Vs, pp);
-                }
-            } else {
-                if (j >= 1 && j - 1 < n_w) pv(Vp, pp);
-                if (j < n_w) softmax_phase(j, Ks, s_cur, s_next);
-            }
-            wait_vm_keep<2 * PERW>();   // K_{j+2} and V_{j+1}, issued one step earlier, have landed
-            barrier_lds();
-        };
-        for (int j = 0; j < n_kv; j += 4) {
-            step(j, K1, V0, V3, K3, V2, sa, sb);
-            if (j + 1 < n_kv) step(j + 1, K2, V1, V0, K0, V3, sb, sa);
-            if (j + 2 < n_kv) step(j + 2, K3, V2, V1, K1, V0, sa, sb);
-            if (j + 3 < n_kv) step(j + 3, K0, V3, V2, K2, V1, sb, sa);
-        }
-        // The late waves' last P V product: V_{n_kv-1} is in buffer
-        // (n_kv-1) % 4 (later copies went to other buffers).
-        if constexpr (LATE) {
-            if (n_w == n_kv) {
-                const int t = (n_kv - 1) & 3;
-                pv(t == 0 ? V0 : t == 1 ? V1 : t == 2 ? V2 : V3, pp);
-            }
-        }
-    };
-    if (late) run(std::true_type{});
-    else run(std::false_type{});
     }
     wait_vm_all();
     }
@@ -890,14 +788,13 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     FwdParams arg = p;
     void* args[] = {&arg};
     if constexpr (D <= 128) {
-        // Dense: 128-row workgroups of 4 waves (three per CU at d = 64, two at
-        // d = 128); block-sparse: 256 rows, 8 waves, one per CU.
-        const int rows = p.bmask ? 256 : 128;
+        // 128-row workgroups of 4 waves: three per CU at d = 64, two at d = 128.
+        const int rows = 128;
         arg.n_qtiles = (p.N + rows - 1) / rows;
         const long grid = (long)p.B * p.Hq * arg.n_qtiles;
         const void* fn;
-        if (p.bmask) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true, 8>);
-        else fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false, 4>);
+        if (p.bmask) fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, true>);
+        else fn = reinterpret_cast<const void*>(&fwd_pipe_kernel<D, CAUSAL, false>);
         return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(2 * rows), args, 0, stream);
     } else {
         arg.n_qtiles = (p.N + 127) / 128;
