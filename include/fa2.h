@@ -240,10 +240,10 @@ fa2_status fa2_bwd_stages_olo(unsigned stages, const void *Q, const void *K, con
  *   block, shared by every batch and head, any alignment.  A zero byte at
  *   (r, c) masks the scores of query rows 128r..128r+127 against keys
  *   128c..128c+127 (set to -inf before the softmax, as the causal mask does;
- *   both apply when causal != 0).  Masked blocks cost no matrix products in
- *   the K/V-tile loop of the backward, nor, at d = 256, anywhere; at d = 64
- *   and 128 the forward and the dQ pass run workgroups of 256 query rows,
- *   which compute the key tiles either of their two mask rows needs.
+ *   both apply when causal != 0).  Masked blocks cost no matrix products:
+ *   every kernel's workgroup covers one mask row (forward, dQ pass) or one
+ *   mask column (the backward's K/V-tile loop) and walks only the blocks it
+ *   keeps.
  *   A query row with no unmasked score gets O = 0 and L = -inf; its dQ is 0
  *   and it adds nothing to dK or dV.
  * Same layouts, workspace, outputs and errors as fa2_fwd / fa2_bwd, for every
