@@ -350,7 +350,7 @@ void fwd_pipe_kernel(const FwdParams p) {
 
     // A block-sparse workgroup may have no tile at all: it only writes O = 0, L = -inf.
     if (!SPARSE || n_kv > 0) {
-    // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0.
+    // ---- prologue: K_0, V_0, K_1 (and, three deep, V_1, K_2) in flight; S_0.
     copy_tile(Kh, tile_at(0), K0);
     copy_tile(Vh, tile_at(0), V0);
     if (1 < n_kv) {
@@ -362,7 +362,7 @@ void fwd_pipe_kernel(const FwdParams p) {
     __syncthreads();
     f32x16 sa[2], sb[2];       // scores of the current and the next tile, alternating
     scores(K0, sa);
-    __syncthreads();          // K_0 is overwritten by K_3 in step 0
+    __syncthreads();          // K_0's buffer is refilled in step 0 (K_3, or K_2 two deep)
 
     {
     // Step j: softmax of S_j (s_cur) with S_{j+1} = K_{j+1} Q^T (into s_next),
