@@ -1736,8 +1736,13 @@ void bwd_kv_kernel(const BwdParams p) {
             for (int k = blk * NS; k < (blk + 1) * NS; ++k) slot(k);
             mask(blk);
         }
+        // At d = 64 two workgroups share a CU: the dV, dK phase runs at raised
+        // wave priority (3-4 % on the K/V loop; priority on the s, dp phase
+        // instead gained 0-3 %).
+        if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int k = NB * NS; k < NP; ++k) slot(k);
+        if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
